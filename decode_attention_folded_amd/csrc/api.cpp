@@ -1,0 +1,332 @@
+// C ABI of libdecode_attn.so (declared in include/decode_attn.h): argument
+// validation, workspace layout, split planning and kernel launches.
+//
+// Every check here runs before anything is enqueued, so a rejected call has no
+// side effect.  This file is plain C++ (no HIP headers); the kernels sit behind
+// the launch functions of kernels.h and report HIP errors as non-zero ints.
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/decode_attn.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxGridDim = 65535;
+constexpr int kTargetWorkgroups = 2048;  // about 8 per CU on a 256-CU part
+constexpr int kMinTilesPerSplit = 8;     // at least 2 tiles per wave
+
+bool is_pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+int log2i(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+struct Shape {
+  int batch, hkv, hq, group, d;
+  int capacity;      // valid-length clamp
+  int stride;        // contiguous slots per (b, kv)
+  bool paged;
+  int page_size;     // paged pool or Quest page size
+  int max_pages;
+};
+
+// Checks shared by the attention entry points.
+int check_cache(const da_kv_cache* kv, int32_t num_q_heads, Shape* s) {
+  if (kv == nullptr) return DA_ERR_NULL;
+  if (kv->batch < 0 || kv->num_kv_heads < 1 || num_q_heads < 1) return DA_ERR_SHAPE;
+  if (kv->batch > kMaxGridDim || kv->num_kv_heads > kMaxGridDim) return DA_ERR_SHAPE;
+  if (num_q_heads % kv->num_kv_heads != 0) return DA_ERR_SHAPE;
+  const int group = num_q_heads / kv->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return DA_ERR_UNSUPPORTED;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return DA_ERR_UNSUPPORTED;
+  s->batch = kv->batch;
+  s->hkv = kv->num_kv_heads;
+  s->hq = num_q_heads;
+  s->group = group;
+  s->d = kv->head_dim;
+  s->paged = kv->page_table != nullptr;
+  s->page_size = kv->page_size;
+  if (s->paged) {
+    if (!is_pow2_in(kv->page_size, 8, 64)) return DA_ERR_UNSUPPORTED;
+    if (kv->max_pages < 1 || kv->num_pages < 1) return DA_ERR_SHAPE;
+    if ((int64_t)kv->max_pages * kv->page_size > INT32_MAX / 2) return DA_ERR_SHAPE;
+    s->max_pages = kv->max_pages;
+    s->capacity = kv->max_pages * kv->page_size;
+    s->stride = 0;
+  } else {
+    if (kv->capacity < 1 || kv->capacity > INT32_MAX / 2) return DA_ERR_SHAPE;
+    s->max_pages = 0;
+    s->capacity = kv->capacity;
+    s->stride = kv->capacity;
+  }
+  return DA_OK;
+}
+
+da::SplitPlan plan_splits(const Shape& s, int max_keys, int num_splits) {
+  da::SplitPlan p;
+  p.keys_per_tile = da::keys_per_tile(s.d, s.group);
+  const int64_t max_tiles = max_keys < 1 ? 1 : (max_keys + p.keys_per_tile - 1) / p.keys_per_tile;
+  int64_t tps;
+  if (num_splits > 0) {
+    tps = (max_tiles + num_splits - 1) / num_splits;
+  } else {
+    const int64_t total = (int64_t)s.batch * s.hkv * max_tiles;
+    tps = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
+  }
+  if (tps < 1) tps = 1;
+  if (tps > da::max_tiles_per_split()) tps = da::max_tiles_per_split();
+  if (tps > max_tiles) tps = max_tiles;
+  p.tiles_per_split = (int32_t)tps;
+  p.max_splits = (int32_t)((max_tiles + tps - 1) / tps);
+  return p;
+}
+
+struct WsLayout {
+  size_t counters, ml, o, total;
+};
+
+WsLayout ws_layout(const Shape& s, const da::SplitPlan& p) {
+  const size_t units = (size_t)s.batch * s.hkv;
+  WsLayout w;
+  w.counters = 0;
+  w.ml = align256(units * sizeof(uint32_t));
+  w.o = w.ml + align256(units * p.max_splits * s.group * 2 * sizeof(float));
+  w.total = w.o + units * p.max_splits * s.group * s.d * sizeof(float);
+  if (w.total == 0) w.total = 256;
+  return w;
+}
+
+// Longest key stream one (b, kv) unit can have: the valid length for dense
+// attention; for the chosen pages, at most budget tokens and at most every
+// page of the sequence (a partial last page still occupies S stream slots).
+int max_stream_keys(const Shape& s, int budget_tokens) {
+  if (budget_tokens <= 0) return s.capacity;
+  const int64_t all_pages = ((int64_t)s.capacity + s.page_size - 1) / s.page_size * s.page_size;
+  return (int)(budget_tokens < all_pages ? budget_tokens : all_pages);
+}
+
+int check_budget(const Shape& s, int budget_tokens) {
+  if (!is_pow2_in(s.page_size, 8, 64)) return DA_ERR_UNSUPPORTED;
+  if (budget_tokens <= 0 || budget_tokens % s.page_size != 0) return DA_ERR_BUDGET;
+  return DA_OK;
+}
+
+int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
+                  const int32_t* page_idx, int32_t budget_tokens, int32_t num_q_heads,
+                  float scale, const void* k_new, const void* v_new, void* out, void* workspace,
+                  size_t workspace_bytes, int32_t num_splits, void* stream) {
+  Shape s;
+  int st = check_cache(kv, num_q_heads, &s);
+  if (st != DA_OK) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return DA_ERR_NULL;
+  if (!isfinite(scale)) return DA_ERR_SHAPE;
+  if (num_splits < 0) return DA_ERR_SHAPE;
+  if (page_idx != nullptr) {
+    st = check_budget(s, budget_tokens);
+    if (st != DA_OK) return st;
+  }
+  if (s.batch == 0) return DA_OK;  // nothing to read or write (empty tensors may be NULL)
+  if (q == nullptr || seqlens == nullptr || out == nullptr || kv->k == nullptr ||
+      kv->v == nullptr)
+    return DA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(kv->k) || !aligned16(kv->v) ||
+      !aligned16(k_new) || !aligned16(v_new))
+    return DA_ERR_SHAPE;
+  const da::SplitPlan plan = plan_splits(s, max_stream_keys(s, page_idx ? budget_tokens : 0),
+                                         num_splits);
+  const WsLayout w = ws_layout(s, plan);
+  if (workspace == nullptr) return DA_ERR_NULL;
+  if (!aligned16(workspace)) return DA_ERR_SHAPE;
+  if (workspace_bytes < w.total) return DA_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  da::AttnLaunch a;
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_table = kv->page_table;
+  a.seqlens = seqlens;
+  a.page_idx = page_idx;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.out = out;
+  a.counters = reinterpret_cast<uint32_t*>(ws + w.counters);
+  a.part_ml = reinterpret_cast<float*>(ws + w.ml);
+  a.part_o = reinterpret_cast<float*>(ws + w.o);
+  a.batch = s.batch;
+  a.num_kv_heads = s.hkv;
+  a.group = s.group;
+  a.head_dim = s.d;
+  a.capacity = s.capacity;
+  a.cache_stride = s.stride;
+  a.page_shift = (s.paged || page_idx) ? log2i(s.page_size) : 0;
+  a.max_pages = s.max_pages;
+  a.num_pages = kv->num_pages;
+  a.num_sel = page_idx ? budget_tokens / s.page_size : 0;
+  a.tiles_per_split = plan.tiles_per_split;
+  a.max_splits = plan.max_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return da::launch_decode(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* da_status_string(int status) {
+  switch (status) {
+    case DA_OK: return "DA_OK";
+    case DA_ERR_NULL: return "DA_ERR_NULL: a required pointer is NULL";
+    case DA_ERR_SHAPE: return "DA_ERR_SHAPE: inconsistent or misaligned arguments";
+    case DA_ERR_UNSUPPORTED: return "DA_ERR_UNSUPPORTED: head_dim, group or page size not supported";
+    case DA_ERR_BUDGET: return "DA_ERR_BUDGET: token budget must be a positive multiple of the page size";
+    case DA_ERR_WORKSPACE: return "DA_ERR_WORKSPACE: workspace too small";
+    case DA_ERR_HIP: return "DA_ERR_HIP: HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int da_workspace_size(const da_kv_cache* kv, int32_t num_q_heads, int32_t budget_tokens,
+                      int32_t num_splits, size_t* bytes_out) {
+  if (bytes_out == nullptr) return DA_ERR_NULL;
+  Shape s;
+  int st = check_cache(kv, num_q_heads, &s);
+  if (st != DA_OK) return st;
+  if (num_splits < 0) return DA_ERR_SHAPE;
+  if (budget_tokens > 0) {
+    st = check_budget(s, budget_tokens);
+    if (st != DA_OK) return st;
+  } else if (budget_tokens < 0) {
+    return DA_ERR_BUDGET;
+  }
+  const da::SplitPlan plan = plan_splits(s, max_stream_keys(s, budget_tokens), num_splits);
+  *bytes_out = ws_layout(s, plan).total;
+  return DA_OK;
+}
+
+int gqa_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
+                    int32_t num_q_heads, float scale, const void* k_new, const void* v_new,
+                    void* out, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                    void* stream) {
+  return run_attention(q, kv, seqlens, nullptr, 0, num_q_heads, scale, k_new, v_new, out,
+                       workspace, workspace_bytes, num_splits, stream);
+}
+
+int quest_sparse_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
+                             const int32_t* page_idx, int32_t budget_tokens,
+                             int32_t num_q_heads, float scale, void* out, void* workspace,
+                             size_t workspace_bytes, int32_t num_splits, void* stream) {
+  if (page_idx == nullptr) return DA_ERR_NULL;
+  return run_attention(q, kv, seqlens, page_idx, budget_tokens, num_q_heads, scale, nullptr,
+                       nullptr, out, workspace, workspace_bytes, num_splits, stream);
+}
+
+int quest_meta_append(const da_kv_cache* kv, void* meta, int32_t meta_max_pages,
+                      const int32_t* seqlens, int32_t n_new, const void* k_new,
+                      const void* v_new, void* stream) {
+  if (kv == nullptr) return DA_ERR_NULL;
+  Shape s;
+  // the group size does not matter for metadata; pass Hq = Hkv
+  int st = check_cache(kv, kv->num_kv_heads, &s);
+  if (st != DA_OK) return st;
+  if (!is_pow2_in(s.page_size, 8, 64)) return DA_ERR_UNSUPPORTED;
+  if ((k_new == nullptr) != (v_new == nullptr)) return DA_ERR_NULL;
+  if (k_new != nullptr && n_new != 1) return DA_ERR_SHAPE;
+  if (n_new < 1) return DA_ERR_SHAPE;
+  if (meta_max_pages < 1 || (int64_t)meta_max_pages * s.page_size < s.capacity)
+    return DA_ERR_SHAPE;
+  if (s.batch == 0) return DA_OK;  // nothing to read or write
+  if (meta == nullptr || seqlens == nullptr || kv->k == nullptr) return DA_ERR_NULL;
+  if (k_new != nullptr && kv->v == nullptr) return DA_ERR_NULL;
+  if (!aligned16(meta) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(k_new) ||
+      !aligned16(v_new))
+    return DA_ERR_SHAPE;
+  const int n = n_new < s.capacity ? n_new : s.capacity;
+  int pages = (n - 1 + s.page_size - 1) / s.page_size + 1;
+  if (pages > meta_max_pages) pages = meta_max_pages;
+  da::MetaLaunch a;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_table = kv->page_table;
+  a.seqlens = seqlens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.meta = meta;
+  a.batch = s.batch;
+  a.num_kv_heads = s.hkv;
+  a.head_dim = s.d;
+  a.capacity = s.capacity;
+  a.cache_stride = s.stride;
+  a.page_shift = log2i(s.page_size);
+  a.max_pages = s.max_pages;
+  a.num_pages = kv->num_pages;
+  a.meta_max_pages = meta_max_pages;
+  a.n_new = n_new;
+  a.pages_per_seq = pages;
+  return da::launch_meta_append(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
+}
+
+int da_quest_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t meta_max_pages,
+                            size_t* bytes_out) {
+  if (bytes_out == nullptr) return DA_ERR_NULL;
+  if (batch < 0 || num_kv_heads < 1 || meta_max_pages < 1) return DA_ERR_SHAPE;
+  *bytes_out = align256((size_t)batch * num_kv_heads * meta_max_pages * sizeof(float));
+  if (*bytes_out == 0) *bytes_out = 256;
+  return DA_OK;
+}
+
+int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_pages,
+                          const int32_t* seqlens, int32_t batch, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                          int32_t budget_tokens, int32_t* page_idx, float* page_scores,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || num_kv_heads < 1 || num_q_heads < 1 || meta_max_pages < 1)
+    return DA_ERR_SHAPE;
+  if (batch > kMaxGridDim || num_kv_heads > kMaxGridDim) return DA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return DA_ERR_SHAPE;
+  const int group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return DA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return DA_ERR_UNSUPPORTED;
+  if (!is_pow2_in(page_size, 8, 64)) return DA_ERR_UNSUPPORTED;
+  if (budget_tokens <= 0 || budget_tokens % page_size != 0) return DA_ERR_BUDGET;
+  if (meta_max_pages > da::topk_max_pages()) return DA_ERR_UNSUPPORTED;
+  if (batch == 0) return DA_OK;  // nothing to read or write
+  if (q == nullptr || meta == nullptr || seqlens == nullptr || page_idx == nullptr)
+    return DA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(meta)) return DA_ERR_SHAPE;
+  float* scores = page_scores;
+  if (scores == nullptr) {
+    size_t need = 0;
+    da_quest_workspace_size(batch, num_kv_heads, meta_max_pages, &need);
+    if (workspace == nullptr) return DA_ERR_NULL;
+    if (!aligned16(workspace)) return DA_ERR_SHAPE;
+    if (workspace_bytes < need) return DA_ERR_WORKSPACE;
+    scores = static_cast<float*>(workspace);
+  }
+  da::ScoreLaunch a;
+  a.q = q;
+  a.meta = meta;
+  a.seqlens = seqlens;
+  a.scores = scores;
+  a.page_idx = page_idx;
+  a.batch = batch;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.head_dim = head_dim;
+  a.page_shift = log2i(page_size);
+  a.meta_max_pages = meta_max_pages;
+  a.num_sel = budget_tokens / page_size;
+  return da::launch_score_topk(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
+}
+
+}  // extern "C"

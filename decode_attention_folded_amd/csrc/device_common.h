@@ -1,0 +1,118 @@
+// Device helpers shared by the gfx950 kernels: fp16 vector types, lane
+// exchanges (DPP, ds_swizzle, ds_bpermute) and small wave/block reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_in_wave() { return threadIdx.x & (kWave - 1); }
+
+// DPP move of a 32-bit value; CTRL is the dpp_ctrl encoding.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// DPP controls used below.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within each 8-lane half row
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within each 16-lane row
+constexpr int kDppRor8 = 0x128;        // lane i <- lane (i+8) mod 16 within each row
+
+// Sum / max over aligned groups of N contiguous lanes (N = 8 or 16).  Every
+// lane of a group ends with the same, bitwise identical value.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  x += dpp_f32<kDppXor1>(x);
+  x += dpp_f32<kDppXor2>(x);
+  x += dpp_f32<kDppHalfMirror>(x);
+  if constexpr (N == 16) x += dpp_f32<kDppMirror>(x);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  x = fmaxf(x, dpp_f32<kDppXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+  if constexpr (N == 16) x = fmaxf(x, dpp_f32<kDppMirror>(x));
+  return x;
+}
+
+// Value of lane (lane ^ MASK) for MASK in {8, 16, 32}.
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float x) {
+  int v = __builtin_bit_cast(int, x);
+  if constexpr (MASK == 8) {
+    v = __builtin_amdgcn_update_dpp(0, v, kDppRor8, 0xF, 0xF, true);
+  } else if constexpr (MASK == 16) {
+    // ds_swizzle bitmask mode: and 0x1f, or 0, xor 0x10 (within 32 lanes)
+    v = __builtin_amdgcn_ds_swizzle(v, (0x10 << 10) | 0x1F);
+  } else {
+    static_assert(MASK == 32, "xor distance 8, 16 or 32");
+    v = __builtin_amdgcn_ds_bpermute((lane_in_wave() ^ 32) << 2, v);
+  }
+  return __builtin_bit_cast(float, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 accumulate of an 8-element fp16 dot product (v_dot2_f32_f16: exact
+// fp16 products, fp32 sums).
+__device__ __forceinline__ float dot8(f16x8 a, f16x8 b, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f16x2 x = {a[2 * i], a[2 * i + 1]};
+    f16x2 y = {b[2 * i], b[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2(x, y, acc, false);
+  }
+  return acc;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = lane_in_wave();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    uint32_t o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a block of NWAVES waves; *total gets the block
+// sum.  Must be reached by every thread of the block.
+template <int NWAVES>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch,
+                                                         uint32_t* total) {
+  const int lane = lane_in_wave();
+  const int wave = threadIdx.x / kWave;
+  const uint32_t inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) {
+    const uint32_t s = scratch[w];
+    if (w < wave) base += s;
+    sum += s;
+  }
+  __syncthreads();
+  *total = sum;
+  return base + inc - v;
+}
+
+}  // namespace da

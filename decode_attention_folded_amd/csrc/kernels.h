@@ -1,0 +1,82 @@
+// Internal launch interface between the C ABI layer (api.cpp, plain C++) and
+// the HIP kernels.  No HIP types appear here so the host layer compiles as
+// ordinary C++.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace da {
+
+// One launch of the split-context decode attention kernel (dense, paged or
+// selected-page key stream).  All pointers are device pointers.
+struct AttnLaunch {
+  const void* q;             // fp16 [B, Hq, D]
+  void* k;                   // fp16 cache [B, Hkv, cap, D] or pool [NP, Hkv, S, D]
+  void* v;
+  const int32_t* page_table; // [B, max_pages] or nullptr (contiguous cache)
+  const int32_t* seqlens;    // [B]
+  const int32_t* page_idx;   // [B, Hkv, num_sel] chosen pages, or nullptr (dense)
+  const void* k_new;         // fp16 [B, Hkv, D] or nullptr
+  const void* v_new;
+  void* out;                 // fp16 [B, Hq, D]
+  uint32_t* counters;        // [B * Hkv], zero between calls
+  float* part_ml;            // [B * Hkv, max_splits, G, 2]
+  float* part_o;             // [B * Hkv, max_splits, G, D]
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t group;             // G = Hq / Hkv
+  int32_t head_dim;          // D
+  int32_t capacity;          // valid-length clamp: cap (contiguous) or max_pages * S
+  int32_t cache_stride;      // slots per (b, kv) row of a contiguous cache
+  int32_t page_shift;        // log2(S) (paged cache and/or selected pages)
+  int32_t max_pages;         // page-table row width
+  int64_t num_pages;         // pool size; page-table entries outside [0, num_pages) are skipped
+  int32_t num_sel;           // K pages per (b, kv) in the selected-page stream
+  int32_t tiles_per_split;   // key tiles per workgroup chunk
+  int32_t max_splits;        // grid.x
+  float scale_log2;          // scale * log2(e)
+};
+
+// Split plan shared by the workspace-size query and the launch.
+struct SplitPlan {
+  int32_t keys_per_tile;
+  int32_t tiles_per_split;
+  int32_t max_splits;
+};
+
+int keys_per_tile(int head_dim, int group);
+int max_tiles_per_split();
+
+int launch_decode(const AttnLaunch& p, void* stream);
+
+struct MetaLaunch {
+  void* k;                   // cache or pool (written only when k_new != nullptr)
+  void* v;
+  const int32_t* page_table;
+  const int32_t* seqlens;
+  const void* k_new;
+  const void* v_new;
+  void* meta;                // fp16 [B, Hkv, meta_max_pages, 2, D]
+  int32_t batch, num_kv_heads, head_dim;
+  int32_t capacity, cache_stride, page_shift, max_pages;
+  int64_t num_pages;
+  int32_t meta_max_pages;
+  int32_t n_new;
+  int32_t pages_per_seq;     // grid.x: pages a single call can touch per sequence
+};
+int launch_meta_append(const MetaLaunch& p, void* stream);
+
+struct ScoreLaunch {
+  const void* q;             // fp16 [B, Hq, D]
+  const void* meta;          // fp16 [B, Hkv, P, 2, D]
+  const int32_t* seqlens;
+  float* scores;             // [B, Hkv, P]
+  int32_t* page_idx;         // [B, Hkv, K]
+  int32_t batch, num_kv_heads, group, head_dim;
+  int32_t page_shift, meta_max_pages, num_sel;
+};
+int launch_score_topk(const ScoreLaunch& p, void* stream);
+int topk_max_pages();
+
+}  // namespace da

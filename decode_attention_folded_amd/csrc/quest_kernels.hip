@@ -1,0 +1,395 @@
+// Quest page metadata, page scores and top-K page selection for gfx950.
+//
+// [Quest-review] "the page score is not an exact attention probability"
+// (paper section 3.4, Algorithm 1):
+//   metadata  m_{p,i} / M_{p,i} = per-channel min / max of the Keys in page p,
+//             updated as each new Key arrives;
+//   score     U(p, q) = sum_i max(q_i m_{p,i}, q_i M_{p,i}), summed here over
+//             the G query heads that share the KV head;
+//   select    the K pages with the largest U (ties to the lower page index),
+//             reported in ascending page order.
+//
+// Kernels:
+//   meta_append_kernel  one wave per (page touched, kv, b); lanes own channel
+//                       pairs; exact fp16 min/max.
+//   page_score_kernel   HBM-bound scan of the metadata: D/8 lanes per page, each
+//                       lane one 16-byte chunk of the min row and of the max
+//                       row.  Because M >= m, max(q m, q M) = q M when q >= 0
+//                       and q m otherwise, so the G heads fold into two fp32
+//                       weight vectors per channel (sum of the non-negative
+//                       and of the negative q_gi) and a page costs 2 FMAs per
+//                       channel instead of 2G.
+//   topk_kernel         one workgroup per (b, kv): scores held in registers as
+//                       order-preserving u32 keys; radix select on 11-bit
+//                       digits below the common prefix of the min and max key,
+//                       then an index-order scan for exact ties and for the
+//                       ascending compaction.  Integer-only decisions, so the
+//                       chosen set is deterministic.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace da {
+namespace {
+
+// ------------------------------------------------------------ metadata
+
+template <int D>
+__global__ void __launch_bounds__(kWave) meta_append_kernel(MetaLaunch a) {
+  const int lane = threadIdx.x;
+  const int kv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int hkv = a.num_kv_heads;
+  const int64_t unit = (int64_t)b * hkv + kv;
+  const int shift = a.page_shift;
+  const int S = 1 << shift;
+
+  int L = a.seqlens[b];
+  L = L < 0 ? 0 : (L > a.capacity ? a.capacity : L);
+  const int n = a.n_new < L ? a.n_new : L;
+  if (n <= 0) return;
+  const int t_lo = L - n;
+  const int p = (t_lo >> shift) + blockIdx.x;
+  if (p >= a.meta_max_pages || (p << shift) >= L) return;
+  const int page_start = p << shift;
+  const int lo = page_start > t_lo ? page_start : t_lo;
+  const int hi = (page_start + S) < L ? (page_start + S) : L;
+  const bool fresh = lo == page_start;
+  if (lane >= D / 2) return;
+
+  f16x2* mp = reinterpret_cast<f16x2*>(reinterpret_cast<f16*>(a.meta) +
+                                       ((unit * a.meta_max_pages + p) * 2) * D);
+  const f16 inf = (f16)__builtin_huge_valf();
+  f16x2 mn = {inf, inf};
+  f16x2 mx = {-inf, -inf};
+  if (!fresh) {
+    mn = mp[lane];
+    mx = mp[D / 2 + lane];
+  }
+  const bool has_new = a.k_new != nullptr;
+  for (int t = lo; t < hi; ++t) {
+    int64_t off;
+    if (a.page_table != nullptr) {
+      const int phys = a.page_table[(int64_t)b * a.max_pages + (t >> shift)];
+      if (phys < 0 || phys >= a.num_pages) continue;  // not a pool page: skip the key
+      off = (((int64_t)phys * hkv + kv) << shift) * D + (int64_t)(t & (S - 1)) * D;
+    } else {
+      off = (unit * a.cache_stride + t) * D;
+    }
+    f16x2 key;
+    if (has_new && t == L - 1) {
+      key = reinterpret_cast<const f16x2*>(reinterpret_cast<const f16*>(a.k_new) + unit * D)[lane];
+      const f16x2 val =
+          reinterpret_cast<const f16x2*>(reinterpret_cast<const f16*>(a.v_new) + unit * D)[lane];
+      reinterpret_cast<f16x2*>(reinterpret_cast<f16*>(a.k) + off)[lane] = key;
+      reinterpret_cast<f16x2*>(reinterpret_cast<f16*>(a.v) + off)[lane] = val;
+    } else {
+      key = reinterpret_cast<const f16x2*>(reinterpret_cast<const f16*>(a.k) + off)[lane];
+    }
+    mn = __builtin_elementwise_min(mn, key);
+    mx = __builtin_elementwise_max(mx, key);
+  }
+  mp[lane] = mn;
+  mp[D / 2 + lane] = mx;
+}
+
+// ------------------------------------------------------------ page score
+
+constexpr int kScoreWaves = 4;
+constexpr int kScoreUnroll = 4;
+
+template <int D>
+struct ScoreShape {
+  static constexpr int LPP = D / 8;                                  // lanes per page
+  static constexpr int PPI = kWave / LPP;                            // pages per wave step
+  static constexpr int PAGES_PER_WG = kScoreWaves * PPI * kScoreUnroll;
+};
+
+template <int D, int G>
+__global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLaunch a) {
+  using SS = ScoreShape<D>;
+  constexpr int LPP = SS::LPP;
+  constexpr int PPI = SS::PPI;
+  const int lane = lane_in_wave();
+  const int wave = threadIdx.x / kWave;
+  const int slot = lane / LPP;  // page within a wave step
+  const int ch = lane % LPP;    // 16-byte chunk of the D channels
+  const int kv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t unit = (int64_t)b * a.num_kv_heads + kv;
+  const int shift = a.page_shift;
+
+  int L = a.seqlens[b];
+  L = L < 0 ? 0 : L;
+  int n_pages = (L + (1 << shift) - 1) >> shift;
+  if (n_pages > a.meta_max_pages) n_pages = a.meta_max_pages;
+  const int p_begin = blockIdx.x * SS::PAGES_PER_WG;
+  if (p_begin >= n_pages) return;
+
+  // Per-channel weights: sum of the group's non-negative q_gi (pairs with the
+  // max) and of its negative q_gi (pairs with the min).
+  float wpos[8], wneg[8];
+  const f16* qb = reinterpret_cast<const f16*>(a.q) + unit * G * D + 8 * ch;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    wpos[e] = 0.0f;
+    wneg[e] = 0.0f;
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const f16x8 qv = *reinterpret_cast<const f16x8*>(qb + g * D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (float)qv[e];
+      if (x >= 0.0f) wpos[e] += x; else wneg[e] += x;
+    }
+  }
+
+  const f16* mbase = reinterpret_cast<const f16*>(a.meta) + unit * a.meta_max_pages * 2 * D;
+  f16x8 mins[kScoreUnroll], maxs[kScoreUnroll];
+  int pg[kScoreUnroll];
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    const int p = p_begin + (u * kScoreWaves + wave) * PPI + slot;
+    pg[u] = p;
+    const int pp = p < n_pages ? p : p_begin;
+    mins[u] = *reinterpret_cast<const f16x8*>(mbase + (int64_t)pp * 2 * D + 8 * ch);
+    maxs[u] = *reinterpret_cast<const f16x8*>(mbase + (int64_t)pp * 2 * D + D + 8 * ch);
+  }
+  float* scores = a.scores + unit * a.meta_max_pages;
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s = fmaf(wpos[e], (float)maxs[u][e], s);
+      s = fmaf(wneg[e], (float)mins[u][e], s);
+    }
+    s = group_sum<LPP>(s);
+    if (ch == 0 && pg[u] < n_pages) scores[pg[u]] = s;
+  }
+}
+
+// ------------------------------------------------------------ top-K
+
+constexpr int kTopkThreads = 256;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kRadixBits = 11;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  // Larger float -> larger key; -0 is folded into +0 first.
+  const uint32_t u = __builtin_bit_cast(uint32_t, f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+enum : uint8_t { kCand = 0, kTake = 1, kDrop = 2 };
+
+template <int R>
+__global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
+  __shared__ uint32_t hist[1 << kRadixBits];
+  __shared__ uint32_t scratch[kTopkWaves];
+  __shared__ uint32_t red_min[kTopkWaves], red_max[kTopkWaves];
+  __shared__ uint32_t info[3];
+
+  const int tid = threadIdx.x;
+  const int kv = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t unit = (int64_t)b * a.num_kv_heads + kv;
+  const int shift_page = a.page_shift;
+  const int K = a.num_sel;
+  int32_t* dst = a.page_idx + unit * K;
+
+  int L = a.seqlens[b];
+  L = L < 0 ? 0 : L;
+  int n_pages = (L + (1 << shift_page) - 1) >> shift_page;
+  if (n_pages > a.meta_max_pages) n_pages = a.meta_max_pages;
+
+  if (n_pages <= K) {  // every existing page is chosen
+    for (int i = tid; i < K; i += kTopkThreads) dst[i] = i < n_pages ? i : -1;
+    return;
+  }
+
+  const float* sc = a.scores + unit * a.meta_max_pages;
+  uint32_t key[R];
+  uint8_t st[R];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = tid * R + j;
+    if (i < n_pages) {
+      key[j] = order_key(sc[i]);
+      st[j] = kCand;
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    } else {
+      key[j] = 0u;
+      st[j] = kDrop;
+    }
+  }
+  // block min / max of the keys
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, kWave));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, kWave));
+  }
+  if (lane_in_wave() == 0) {
+    red_min[tid / kWave] = kmin;
+    red_max[tid / kWave] = kmax;
+  }
+  __syncthreads();
+  kmin = red_min[0];
+  kmax = red_max[0];
+#pragma unroll
+  for (int w = 1; w < kTopkWaves; ++w) {
+    kmin = min(kmin, red_min[w]);
+    kmax = max(kmax, red_max[w]);
+  }
+  const uint32_t diff = kmin ^ kmax;
+  int shift = diff ? 32 - __builtin_clz(diff) : 0;  // bits below the common prefix
+
+  uint32_t need = (uint32_t)K;          // pages still to choose
+  uint32_t ncand = (uint32_t)n_pages;   // candidates: same key prefix above `shift`
+  while (need > 0 && need < ncand && shift > 0) {
+    const int nb = shift < kRadixBits ? shift : kRadixBits;
+    shift -= nb;
+    const uint32_t nbins = 1u << nb;
+    for (uint32_t i = tid; i < nbins; i += kTopkThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (st[j] == kCand) atomicAdd(&hist[(key[j] >> shift) & (nbins - 1)], 1u);
+    __syncthreads();
+    // Thread t sums a run of `per` digits, taken from the top digit down.
+    const int per = (int)((nbins + kTopkThreads - 1) / kTopkThreads);
+    uint32_t run = 0;
+    for (int q = 0; q < per; ++q) {
+      const int dgt = (int)nbins - 1 - (tid * per + q);
+      if (dgt >= 0) run += hist[dgt];
+    }
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan<kTopkWaves>(run, scratch, &total);
+    if (before < need && need <= before + run) {
+      uint32_t acc = before;
+      for (int q = 0; q < per; ++q) {
+        const int dgt = (int)nbins - 1 - (tid * per + q);
+        if (dgt < 0) break;
+        const uint32_t cnt = hist[dgt];
+        if (acc + cnt >= need) {
+          info[0] = (uint32_t)dgt;  // boundary digit
+          info[1] = acc;            // candidates above it
+          info[2] = cnt;            // candidates on it
+          break;
+        }
+        acc += cnt;
+      }
+    }
+    __syncthreads();
+    const uint32_t dstar = info[0];
+    const uint32_t above = info[1];
+    const uint32_t on = info[2];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (st[j] == kCand) {
+        const uint32_t dg = (key[j] >> shift) & (nbins - 1);
+        if (dg > dstar) st[j] = kTake;
+        else if (dg < dstar) st[j] = kDrop;
+      }
+    }
+    need -= above;
+    ncand = on;
+    __syncthreads();
+  }
+
+  // Remaining candidates: all taken if they fit; otherwise their keys are
+  // equal and the lowest page indices win.
+  {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) mine += st[j] == kCand;
+    uint32_t total;
+    uint32_t rank = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (st[j] == kCand) {
+        st[j] = rank < need ? kTake : kDrop;
+        ++rank;
+      }
+    }
+  }
+
+  // Ascending compaction of the chosen pages.
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) mine += st[j] == kTake;
+  uint32_t total;
+  uint32_t pos = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (st[j] == kTake) {
+      if (pos < (uint32_t)K) dst[pos] = tid * R + j;
+      ++pos;
+    }
+  }
+  for (uint32_t i = total + tid; i < (uint32_t)K; i += kTopkThreads) dst[i] = -1;
+}
+
+template <int D, int G>
+int launch_score(const ScoreLaunch& a, hipStream_t s) {
+  const int per_wg = ScoreShape<D>::PAGES_PER_WG;
+  dim3 grid((a.meta_max_pages + per_wg - 1) / per_wg, a.num_kv_heads, a.batch);
+  hipLaunchKernelGGL((page_score_kernel<D, G>), grid, dim3(kWave * kScoreWaves), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int launch_score_d(const ScoreLaunch& a, hipStream_t s) {
+  switch (a.group) {
+    case 1: return launch_score<D, 1>(a, s);
+    case 2: return launch_score<D, 2>(a, s);
+    case 4: return launch_score<D, 4>(a, s);
+    case 8: return launch_score<D, 8>(a, s);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+template <int R>
+int launch_topk(const ScoreLaunch& a, hipStream_t s) {
+  dim3 grid(a.num_kv_heads, a.batch);
+  hipLaunchKernelGGL((topk_kernel<R>), grid, dim3(kTopkThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_meta_append(const MetaLaunch& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dim3 grid(a.pages_per_seq, a.num_kv_heads, a.batch);
+  if (a.head_dim == 64) {
+    hipLaunchKernelGGL((meta_append_kernel<64>), grid, dim3(kWave), 0, s, a);
+  } else if (a.head_dim == 128) {
+    hipLaunchKernelGGL((meta_append_kernel<128>), grid, dim3(kWave), 0, s, a);
+  } else {
+    return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_score_topk(const ScoreLaunch& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int err = a.head_dim == 64 ? launch_score_d<64>(a, s)
+          : a.head_dim == 128 ? launch_score_d<128>(a, s)
+                              : (int)hipErrorInvalidValue;
+  if (err != 0) return err;
+  const int P = a.meta_max_pages;
+  if (P <= kTopkThreads * 8) return launch_topk<8>(a, s);
+  if (P <= kTopkThreads * 32) return launch_topk<32>(a, s);
+  if (P <= kTopkThreads * 64) return launch_topk<64>(a, s);
+  return (int)hipErrorInvalidValue;
+}
+
+int topk_max_pages() { return kTopkThreads * 64; }
+
+}  // namespace da

@@ -1,0 +1,202 @@
+/*
+ * decode_attn.h -- C ABI of libdecode_attn.so: folded-GQA single-token decode
+ * attention and the Quest query-aware sparse variant, for AMD MI355X (gfx950).
+ *
+ * Sources, cited by page and section:
+ *   [CoreML-GQA]   "Core ML Decode Optimization: Removing the 1.9 GiB Per-Token
+ *                  Copy Caused by GQA repeat_kv" (OptAI engineering blog).
+ *   [Quest-review] jaehun.me review of "Quest: Query-Aware Sparsity for
+ *                  Efficient Long-Context LLM Inference" (paper sections 3.3-3.5,
+ *                  Algorithm 1 as the review cites them).
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are HIP device pointers; (host) are host memory.
+ *   - fp16 means IEEE binary16; every tensor is contiguous, row-major, last
+ *     axis fastest.  fp16 is the only element type for Q, K, V and outputs.
+ *   - Query head h belongs to KV head h / G with G = Hq / Hkv, i.e. the heads
+ *     of one group are contiguous (h = G*kv + g).  [CoreML-GQA] section 3 "Why
+ *     Reshape Replaces Integer Division"; interleaved head orders (section 5)
+ *     are outside the contract and cannot be detected.
+ *   - seqlens (device, int32 [B]) holds the valid length L_b of each sequence,
+ *     *including* the token appended this step.  Values are clamped on the
+ *     device to [0, capacity]; L_b = 0 yields an all-zero output row.
+ *   - The caller owns every buffer, including the workspace.  The library never
+ *     allocates, frees or synchronises, and keeps no pointer after returning.
+ *     All work is enqueued on `stream` (a hipStream_t; NULL = null stream) and
+ *     is complete after the caller synchronises that stream.
+ *   - Workspace: size it with da_workspace_size / da_quest_workspace_size,
+ *     zero-fill it once before its first use (it holds split counters that
+ *     every completed call leaves at zero again), and do not share one
+ *     workspace between calls that may run concurrently.
+ *   - Return value: DA_OK or a negative DA_ERR_* code.  All argument checks run
+ *     before anything is enqueued; only DA_ERR_HIP can follow a partial enqueue.
+ *     The library never prints and never aborts.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum da_status {
+  DA_OK = 0,
+  DA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  DA_ERR_SHAPE = -2,       /* inconsistent sizes (Hq % Hkv != 0, capacity < 1, ...) */
+  DA_ERR_UNSUPPORTED = -3, /* D not in {64,128}, G not in {1,2,4,8}, S not in {8,16,32,64} */
+  DA_ERR_BUDGET = -4,      /* token budget not a positive multiple of S          */
+  DA_ERR_WORKSPACE = -5,   /* workspace too small                                */
+  DA_ERR_HIP = -6          /* a HIP launch or query failed (e.g. no device)      */
+};
+
+/*
+ * A KV cache, described on the host (the struct itself is host memory).
+ *
+ * Contiguous (page_table == NULL):
+ *   k, v      (device) fp16 [batch, num_kv_heads, capacity, head_dim].
+ *   page_size  Quest metadata page size S (only read by the quest_* calls).
+ * Paged (page_table != NULL):
+ *   k, v      (device) fp16 pool [num_pages, num_kv_heads, page_size, head_dim].
+ *   page_table (device) int32 [batch, max_pages]: token t of sequence b is row
+ *              (t mod S) of pool page page_table[b][t / S].  Entries for pages
+ *              that hold a valid token must lie in [0, num_pages); this is a
+ *              precondition the device cannot check.
+ *   capacity   is ignored; the per-sequence capacity is max_pages * page_size.
+ * k and v are written only by calls that append a row (k_new/v_new != NULL).
+ */
+typedef struct da_kv_cache {
+  void* k;
+  void* v;
+  const int32_t* page_table;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+  int32_t page_size;
+  int32_t max_pages;
+  int64_t num_pages;
+} da_kv_cache;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* da_status_string(int status);
+
+/*
+ * Workspace bytes for gqa_decode_attn (budget_tokens == 0) or
+ * quest_sparse_decode_attn (budget_tokens > 0, the token budget K*S) on this
+ * cache with num_q_heads query heads and the given num_splits (0 = automatic).
+ * Writes the size to *bytes_out (host).  The split heuristic depends only on
+ * these arguments, so a workspace sized once can be reused for every call with
+ * the same shapes.
+ */
+int da_workspace_size(const da_kv_cache* kv, int32_t num_q_heads, int32_t budget_tokens,
+                      int32_t num_splits, size_t* bytes_out);
+
+/*
+ * Folded GQA decode attention.  [CoreML-GQA] section 3 "Fold Q Instead of
+ * Expanding KV" / "Implementation": Q [B, Hq, D] is read as [B, Hkv, G, D], so
+ * every K/V row is read from HBM once for the G query heads that share it (no
+ * repeat_kv copy); scores = scale * q.k over t < L_b, softmax over the context
+ * axis, out = prob . V, written back as [B, Hq, D].
+ *
+ *   q          (device) fp16 [B, Hq, D]
+ *   kv         (host)   cache description (contiguous or paged)
+ *   seqlens    (device) int32 [B]
+ *   num_q_heads Hq; Hq % Hkv == 0 and G = Hq / Hkv in {1, 2, 4, 8}
+ *   scale      multiplier on q.k (1/sqrt(D) for standard attention)
+ *   k_new, v_new (device) fp16 [B, Hkv, D] or both NULL.  When given, the row
+ *              is first stored at slot L_b - 1 of the cache ([CoreML-GQA]
+ *              section 1: one position per token) and attention covers
+ *              [0, L_b) including it.  Skipped for sequences with L_b = 0.
+ *   out        (device) fp16 [B, Hq, D]
+ *   workspace  (device) >= da_workspace_size(kv, Hq, 0, num_splits) bytes
+ *   num_splits 0 = automatic; otherwise the number of context chunks per
+ *              (b, kv) unit for the longest possible sequence.
+ */
+int gqa_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
+                    int32_t num_q_heads, float scale, const void* k_new, const void* v_new,
+                    void* out, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                    void* stream);
+
+/*
+ * Quest metadata update.  [Quest-review] "the page score is not an exact
+ * attention probability" (paper section 3.4): per page p and channel i keep
+ * the Key minimum m_{p,i} and maximum M_{p,i}, updated as new Keys arrive.
+ *
+ *   kv         (host)   cache description; S = kv->page_size in {8,16,32,64}
+ *   meta       (device) fp16 [B, Hkv, meta_max_pages, 2, D]; [...,0,:] = min,
+ *              [...,1,:] = max.  meta_max_pages * S >= per-sequence capacity.
+ *   seqlens    (device) int32 [B] (lengths after this update)
+ *   n_new      keys [L_b - n_new, L_b) are folded in, in order.  A key at a
+ *              page start (t mod S == 0) resets that page to (k, k); any other
+ *              key lowers the min and raises the max.  n_new = 1 is the decode
+ *              step; n_new >= capacity rebuilds every page from the cache.
+ *   k_new, v_new (device) fp16 [B, Hkv, D] or both NULL.  When given, n_new
+ *              must be 1 and the row is also stored at slot L_b - 1 of the
+ *              cache (so a following sparse attention call sees it).
+ * The update is exact (min/max of fp16 values) and idempotent for n_new = 1.
+ */
+int quest_meta_append(const da_kv_cache* kv, void* meta, int32_t meta_max_pages,
+                      const int32_t* seqlens, int32_t n_new, const void* k_new,
+                      const void* v_new, void* stream);
+
+/*
+ * Quest workspace bytes for quest_page_score_topk (page scores of every
+ * (b, kv) unit when the caller passes page_scores = NULL).
+ */
+int da_quest_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t meta_max_pages,
+                            size_t* bytes_out);
+
+/*
+ * Quest page scores and top-K pages.  [Quest-review] (paper section 3.4,
+ * Algorithm 1): U(p, q) = sum_i max(q_i m_{p,i}, q_i M_{p,i}); keep the K pages
+ * with the highest U.  With G > 1 query heads per KV head the score of a page
+ * is the sum of U over the G heads of the group, and one page set per (b, kv)
+ * serves all of them.  No softmax scale is applied (the ranking is invariant
+ * to a common positive scale).
+ *
+ *   q          (device) fp16 [B, Hq, D]
+ *   meta       (device) fp16 [B, Hkv, meta_max_pages, 2, D] (quest_meta_append)
+ *   seqlens    (device) int32 [B]; pages p < ceil(L_b / S) exist
+ *   page_size  S in {8, 16, 32, 64}
+ *   budget_tokens  B = K * S tokens ([Quest-review] "distinguish page count
+ *              from token budget"); must be a positive multiple of S.
+ *   page_idx   (device) int32 [B, Hkv, K] out: the min(K, P_b) chosen pages in
+ *              ascending page order, then -1.  Ties in U go to the lower index.
+ *   page_scores (device) fp32 [B, Hkv, meta_max_pages] out, or NULL to keep the
+ *              scores in the workspace.  Entries p >= P_b are not written.
+ *   workspace  (device) >= da_quest_workspace_size(...) bytes when
+ *              page_scores is NULL (may be NULL otherwise)
+ * Supports meta_max_pages <= 16384.
+ */
+int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_pages,
+                          const int32_t* seqlens, int32_t batch, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                          int32_t budget_tokens, int32_t* page_idx, float* page_scores,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention over the chosen pages only.  [Quest-review] flowchart and worked
+ * example (paper sections 3.3-3.5): exact attention over the real K/V of the
+ * tokens in the chosen pages, [p*S, min(p*S + S, L_b)) for every p in
+ * page_idx[b][kv], folded across the G query heads of the group; the softmax
+ * renormalises over those tokens.
+ *
+ *   page_idx   (device) int32 [B, Hkv, K] as written by quest_page_score_topk
+ *              (ascending, -1 padded); K = budget_tokens / kv->page_size
+ *   other arguments as gqa_decode_attn (no append: use quest_meta_append's
+ *   k_new/v_new for the step's row).  A paged cache must use the same page
+ *   size as the metadata.
+ */
+int quest_sparse_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
+                             const int32_t* page_idx, int32_t budget_tokens,
+                             int32_t num_q_heads, float scale, void* out, void* workspace,
+                             size_t workspace_bytes, int32_t num_splits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

@@ -1,0 +1,419 @@
+"""GPU parity: the HIP path, called through the C ABI binding, against the
+fp64 CPU oracle on the same seeded fp16 inputs.
+
+Bars (stated here and in the design notes):
+* attention outputs: max |gpu - oracle| <= 2e-3 (fp16 inputs, fp32
+  accumulation, fp16 output);
+* metadata: bit-exact (min/max of fp16 values);
+* page scores: |gpu - oracle| <= 2e-6 * sum_i |w_i| |extreme_i| (a bound on
+  fp32 accumulation of 2D products with at most ~25 roundings each);
+* chosen pages: identical, except that a page may be swapped for another
+  when both oracle scores lie within 1e-5 relative of the oracle's K-th
+  score; the GPU choice must also be an exact top-K of its own fp32 scores.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import quest as oquest
+from decode_attention_folded_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-3
+DEV = "cuda:0"
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def da():
+    import decode_attention_folded_amd as pkg
+    pkg.load_library()
+    return pkg
+
+
+def run_dense(da, case, num_splits=0, with_new=False):
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    kn = vn = None
+    if with_new:
+        kn, vn = dev(case.k_new), dev(case.v_new)
+    pt = dev(case.page_table) if case.page_table is not None else None
+    out = da.gqa_decode_attn(q, k, v, dev(case.seqlens), k_new=kn, v_new=vn, page_table=pt,
+                             page_size=case.page_size, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return host(out).astype(np.float64), k, v
+
+
+def max_err(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+# ------------------------------------------------------------ dense attention
+
+DENSE_SHAPES = [
+    # (D, G, Hkv, cap, lengths)
+    (64, 4, 8, 1100, [1100, 517, 1]),
+    (64, 1, 4, 700, [700, 16, 17]),
+    (64, 2, 2, 400, [15, 400, 399]),
+    (64, 8, 2, 600, [600, 333]),
+    (128, 4, 8, 1100, [1100, 517, 1]),
+    (128, 1, 4, 700, [700, 16, 17]),
+    (128, 2, 2, 400, [15, 400, 399]),
+    (128, 8, 2, 600, [600, 333, 8, 9]),
+]
+
+
+@pytest.mark.parametrize("d,g,hkv,cap,lens", DENSE_SHAPES)
+def test_dense_parity(da, d, g, hkv, cap, lens):
+    case = workloads.dense_case(100 + d + g, len(lens), hkv * g, hkv, d, cap, lens)
+    got, _, _ = run_dense(da, case)
+    want = oracle.decode_attention(case.q, case.k, case.v, case.seqlens, case.scale)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, want) <= ATOL
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64])
+def test_dense_split_counts(da, splits):
+    case = workloads.dense_case(7, 2, 32, 8, 128, 2000, [2000, 1234])
+    got, _, _ = run_dense(da, case, num_splits=splits)
+    want = oracle.decode_attention(case.q, case.k, case.v, case.seqlens, case.scale)
+    assert max_err(got, want) <= ATOL
+
+
+def test_dense_bitwise_deterministic(da):
+    case = workloads.dense_case(8, 2, 32, 8, 128, 3000, [3000, 2047])
+    a, _, _ = run_dense(da, case)
+    b, _, _ = run_dense(da, case)
+    assert np.array_equal(a, b)
+
+
+def test_dense_append(da):
+    """Fused append: the new row lands at slot L_b - 1, attention includes it."""
+    lens = [1000, 17, 1]
+    case = workloads.dense_case(9, 3, 32, 8, 64, 1024, lens, with_new=True)
+    got, k_dev, v_dev = run_dense(da, case, with_new=True)
+    k2, v2 = oracle.append_kv(case.k, case.v, case.seqlens, case.k_new, case.v_new)
+    want = oracle.decode_attention(case.q, k2, v2, case.seqlens, case.scale)
+    assert max_err(got, want) <= ATOL
+    kh, vh = host(k_dev), host(v_dev)
+    for b, lb in enumerate(lens):
+        assert np.array_equal(kh[b, :, lb - 1], case.k_new[b])
+        assert np.array_equal(vh[b, :, lb - 1], case.v_new[b])
+        assert np.array_equal(kh[b, :, :lb - 1], case.k[b, :, :lb - 1])
+
+
+def test_dense_empty_and_zero_batch(da):
+    case = workloads.dense_case(10, 3, 8, 2, 64, 64, [0, 5, 0])
+    got, _, _ = run_dense(da, case)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    want = oracle.decode_attention(case.q, case.k, case.v, case.seqlens, case.scale)
+    assert max_err(got, want) <= ATOL
+    q = torch.zeros((0, 8, 64), dtype=torch.float16, device=DEV)
+    k = torch.zeros((0, 2, 64, 64), dtype=torch.float16, device=DEV)
+    out = da.gqa_decode_attn(q, k, k, torch.zeros(0, dtype=torch.int32, device=DEV))
+    assert out.shape == (0, 8, 64)
+
+
+def test_dense_single_key_is_exact(da):
+    case = workloads.dense_case(11, 2, 32, 8, 128, 64, [1, 1])
+    got, _, _ = run_dense(da, case)
+    for h in range(32):
+        assert np.array_equal(got[:, h], case.v[:, h // 4, 0].astype(np.float64))
+
+
+def test_fold_equals_materialised_repeat_kv(da):
+    """The fold on [B, Hkv, G, D] against the same library at G = 1 on an
+    explicitly repeated cache (the page's repeat_kv form)."""
+    case = workloads.dense_case(12, 2, 32, 8, 128, 900, [900, 300])
+    got, _, _ = run_dense(da, case)
+    rep = workloads.Case(q=case.q, k=np.repeat(case.k, 4, axis=1), v=np.repeat(case.v, 4, axis=1),
+                         seqlens=case.seqlens, num_kv_heads=32, head_dim=128, capacity=900)
+    got_rep, _, _ = run_dense(da, rep)
+    assert max_err(got, got_rep) <= ATOL
+
+
+@pytest.mark.parametrize("page_size", [8, 16, 32, 64])
+@pytest.mark.parametrize("d,g", [(128, 4), (64, 4), (128, 8), (64, 1)])
+def test_paged_parity(da, page_size, d, g):
+    hkv, max_pages = 4, (1500 + page_size - 1) // page_size
+    lens = [1500, 37, 1, page_size * 3]
+    case = workloads.paged_case(200 + page_size + d + g, len(lens), hkv * g, hkv, d, page_size,
+                                max_pages, lens, spare_pages=3)
+    got, _, _ = run_dense(da, case)
+    kc = oracle.gather_paged(case.k, case.page_table, page_size, case.capacity)
+    vc = oracle.gather_paged(case.v, case.page_table, page_size, case.capacity)
+    want = oracle.decode_attention(case.q, kc, vc, case.seqlens, case.scale)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, want) <= ATOL
+
+
+# ------------------------------------------------------------ quest metadata
+
+
+def run_meta_bulk(da, case, page_size, max_pages):
+    meta = torch.zeros((case.batch, case.num_kv_heads, max_pages, 2, case.head_dim),
+                       dtype=torch.float16, device=DEV)
+    k, v = dev(case.k), dev(case.v)
+    pt = dev(case.page_table) if case.page_table is not None else None
+    da.quest_meta_append(k, v, meta, dev(case.seqlens), n_new=case.capacity,
+                         page_size=page_size, page_table=pt)
+    torch.cuda.synchronize()
+    return meta
+
+
+@pytest.mark.parametrize("page_size", [8, 16, 64])
+@pytest.mark.parametrize("d", [64, 128])
+def test_metadata_bulk_bit_exact(da, page_size, d):
+    lens = [1000, 33, 1, 64]
+    cap = 1024
+    case = workloads.dense_case(300 + page_size, len(lens), 8, 2, d, cap, lens)
+    max_pages = cap // page_size
+    meta = host(run_meta_bulk(da, case, page_size, max_pages))
+    want = oquest.build_metadata(case.k, case.seqlens, page_size, max_pages)
+    for b, lb in enumerate(lens):
+        n = oquest.page_count(lb, page_size)
+        assert np.array_equal(meta[b, :, :n], want[b, :, :n])
+
+
+def test_metadata_step_append_matches_bulk(da):
+    """Token-by-token append with the fused cache write equals the bulk build,
+    bit for bit, and writes the rows into the cache."""
+    page_size, cap, d = 16, 80, 128
+    case = workloads.dense_case(310, 2, 8, 2, d, cap, [cap, cap], poison=False)
+    k = torch.zeros_like(dev(case.k))
+    v = torch.zeros_like(dev(case.v))
+    meta = torch.zeros((2, 2, cap // page_size, 2, d), dtype=torch.float16, device=DEV)
+    for step in range(1, 71):
+        lens = dev(np.array([step, max(1, step - 5)], np.int32))
+        kn = dev(np.stack([case.k[0, :, step - 1], case.k[1, :, max(1, step - 5) - 1]]))
+        vn = dev(np.stack([case.v[0, :, step - 1], case.v[1, :, max(1, step - 5) - 1]]))
+        da.quest_meta_append(k, v, meta, lens, 1, page_size=page_size, k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    final = np.array([70, 65], np.int32)
+    want = oquest.build_metadata(case.k, final, page_size, cap // page_size)
+    got = host(meta)
+    for b in range(2):
+        n = oquest.page_count(final[b], page_size)
+        assert np.array_equal(got[b, :, :n], want[b, :, :n])
+        assert np.array_equal(host(k)[b, :, :final[b]], case.k[b, :, :final[b]])
+        assert np.array_equal(host(v)[b, :, :final[b]], case.v[b, :, :final[b]])
+
+
+def test_metadata_paged(da):
+    page_size, d = 16, 128
+    lens = [500, 16, 3]
+    case = workloads.paged_case(320, 3, 8, 2, d, page_size, 40, lens)
+    meta = host(run_meta_bulk(da, case, page_size, 40))
+    kc = oracle.gather_paged(case.k, case.page_table, page_size, case.capacity)
+    want = oquest.build_metadata(kc, case.seqlens, page_size, 40)
+    for b, lb in enumerate(lens):
+        n = oquest.page_count(lb, page_size)
+        assert np.array_equal(meta[b, :, :n], want[b, :, :n])
+
+
+# ------------------------------------------------------------ scores and top-K
+
+
+def check_selection(gpu_idx, gpu_scores, want_idx, want_scores, seqlens, page_size, k_pages):
+    """Compare chosen pages under the near-tie rule; also check the GPU set is
+    an exact top-K (ties to lower index) of its own fp32 scores."""
+    bsz, hkv, _ = gpu_idx.shape
+    swaps = 0
+    for b in range(bsz):
+        n = oquest.page_count(seqlens[b], page_size)
+        for kv in range(hkv):
+            g = [int(p) for p in gpu_idx[b, kv] if p >= 0]
+            w = [int(p) for p in want_idx[b, kv] if p >= 0]
+            assert g == sorted(g) and len(g) == min(k_pages, n)
+            assert list(gpu_idx[b, kv, len(g):]) == [-1] * (k_pages - len(g))
+            if g != w:
+                ws = want_scores[b, kv, :n]
+                kth = np.sort(ws)[::-1][min(k_pages, n) - 1]
+                for p in set(g) ^ set(w):
+                    assert abs(ws[p] - kth) <= 1e-5 * abs(kth), (b, kv, p, ws[p], kth)
+                swaps += len(set(g) ^ set(w)) // 2
+            if gpu_scores is not None and n > k_pages:
+                s = gpu_scores[b, kv, :n]
+                chosen = set(g)
+                worst = min((s[p], -p) for p in chosen)
+                best_out = max(((s[p], -p) for p in range(n) if p not in chosen))
+                assert worst > best_out
+    return swaps
+
+
+def score_tolerance(q, meta, seqlens, page_size):
+    """2e-6 * sum_i |w+_i| |M_i| + |w-_i| |m_i| per page."""
+    q64 = q.astype(np.float64)
+    bsz, hq, d = q64.shape
+    hkv = meta.shape[1]
+    g = hq // hkv
+    tol = np.zeros(meta.shape[:3])
+    for b in range(bsz):
+        for kv in range(hkv):
+            qs = q64[b, kv * g:(kv + 1) * g]
+            wpos = np.where(qs >= 0, qs, 0).sum(0)
+            wneg = np.where(qs < 0, qs, 0).sum(0)
+            mag = (np.abs(meta[b, kv, :, 1].astype(np.float64)) @ np.abs(wpos)
+                   + np.abs(meta[b, kv, :, 0].astype(np.float64)) @ np.abs(wneg))
+            tol[b, kv] = 2e-6 * mag + 1e-30
+    return tol
+
+
+@pytest.mark.parametrize("page_size,budget,g,d,cap,lens", [
+    (16, 256, 4, 128, 4096, [4096, 1000, 200, 17]),
+    (16, 64, 1, 128, 2048, [2048, 2047]),
+    (8, 64, 2, 64, 1024, [1024, 900]),
+    (32, 512, 8, 128, 8192, [8192, 5000]),
+    (64, 128, 4, 64, 4096, [4096, 100]),
+    (16, 2048, 4, 128, 32768, [32768]),
+])
+def test_score_topk_parity(da, page_size, budget, g, d, cap, lens):
+    hkv = 2
+    case = workloads.dense_case(400 + page_size + g, len(lens), hkv * g, hkv, d, cap, lens,
+                                plant_pages=4, plant_page_size=page_size)
+    max_pages = cap // page_size
+    k_pages = budget // page_size
+    meta_dev = run_meta_bulk(da, case, page_size, max_pages)
+    meta = host(meta_dev)
+    scores = torch.full((len(lens), hkv, max_pages), float("nan"), dtype=torch.float32,
+                        device=DEV)
+    idx = da.quest_page_score_topk(dev(case.q), meta_dev, dev(case.seqlens), page_size=page_size,
+                                   budget_tokens=budget, page_scores=scores)
+    torch.cuda.synchronize()
+    want_meta = oquest.build_metadata(case.k, case.seqlens, page_size, max_pages)
+    want_scores = oquest.page_scores(case.q, want_meta, case.seqlens, page_size)
+    want_idx = oquest.select_pages(want_scores, case.seqlens, page_size, k_pages)
+    got_scores = host(scores).astype(np.float64)
+    tol = score_tolerance(case.q, want_meta, case.seqlens, page_size)
+    for b, lb in enumerate(lens):
+        n = oquest.page_count(lb, page_size)
+        assert np.all(np.abs(got_scores[b, :, :n] - want_scores[b, :, :n]) <= tol[b, :, :n])
+    check_selection(host(idx), got_scores, want_idx, want_scores, case.seqlens, page_size,
+                    k_pages)
+    # the same call without a score buffer uses the workspace and agrees
+    idx2 = da.quest_page_score_topk(dev(case.q), meta_dev, dev(case.seqlens),
+                                    page_size=page_size, budget_tokens=budget)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx2), host(idx))
+
+
+def test_topk_exact_ties_lower_index(da):
+    """Pages with identical keys tie exactly in fp32 too; the lower index is
+    chosen.  Many ties straddle the K-th position here."""
+    page_size, cap, d = 16, 2048, 128
+    case = workloads.dense_case(410, 1, 4, 1, d, cap, [cap], poison=False)
+    # 40 copies of one page, pushed along the sign of the summed query so they
+    # outscore every other page; K = 24 must then split the tied copies
+    qsum = case.q[0].astype(np.float32).sum(axis=0)
+    hot = (case.k[0, 0, 0:16].astype(np.float32) + 2.0 * np.sign(qsum)).astype(np.float16)
+    copies = list(range(3, 128, 3))[:40]
+    for p in copies:
+        case.k[0, 0, p * 16:(p + 1) * 16] = hot
+    meta_dev = run_meta_bulk(da, case, page_size, cap // page_size)
+    idx = host(da.quest_page_score_topk(dev(case.q), meta_dev, dev(case.seqlens),
+                                        page_size=page_size, budget_tokens=24 * 16))
+    want_meta = oquest.build_metadata(case.k, case.seqlens, page_size, cap // page_size)
+    want_scores = oquest.page_scores(case.q, want_meta, case.seqlens, page_size)
+    want = oquest.select_pages(want_scores, case.seqlens, page_size, 24)
+    assert np.array_equal(idx, want)
+
+
+def test_topk_fewer_pages_than_budget(da):
+    case = workloads.dense_case(420, 2, 8, 2, 128, 512, [100, 512])
+    meta_dev = run_meta_bulk(da, case, 16, 32)
+    idx = host(da.quest_page_score_topk(dev(case.q), meta_dev, dev(case.seqlens), page_size=16,
+                                        budget_tokens=64 * 16))
+    assert list(idx[0, 0, :7]) == list(range(7)) and np.all(idx[0, :, 7:] == -1)
+    assert list(idx[1, 1, :32]) == list(range(32)) and np.all(idx[1, :, 32:] == -1)
+
+
+# ------------------------------------------------------------ sparse attention
+
+
+@pytest.mark.parametrize("page_size,budget,g,d,lens", [
+    (16, 256, 4, 128, [4096, 1000, 200, 17]),
+    (16, 2048, 1, 128, [2048, 2047]),
+    (8, 64, 2, 64, [1024, 900]),
+    (32, 512, 8, 128, [3000, 64]),
+    (64, 128, 4, 64, [4096, 100]),
+])
+def test_sparse_parity(da, page_size, budget, g, d, lens):
+    hkv, cap = 2, max(lens)
+    cap = ((cap + 63) // 64) * 64
+    case = workloads.dense_case(500 + page_size + g, len(lens), hkv * g, hkv, d, cap, lens,
+                                plant_pages=4, plant_page_size=page_size)
+    k_pages = budget // page_size
+    meta = oquest.build_metadata(case.k, case.seqlens, page_size, cap // page_size)
+    idx = oquest.select_pages(oquest.page_scores(case.q, meta, case.seqlens, page_size),
+                              case.seqlens, page_size, k_pages)
+    out = da.quest_sparse_decode_attn(dev(case.q), dev(case.k), dev(case.v), dev(case.seqlens),
+                                      dev(idx), budget_tokens=budget, page_size=page_size)
+    torch.cuda.synchronize()
+    want = oquest.sparse_decode_attention(case.q, case.k, case.v, case.seqlens, idx, page_size,
+                                          case.scale)
+    assert max_err(host(out), want) <= ATOL
+
+
+def test_sparse_all_pages_equals_dense(da):
+    lens = [1000, 333]
+    case = workloads.dense_case(510, 2, 32, 8, 128, 1024, lens)
+    idx = np.full((2, 8, 64), -1, np.int32)
+    for b, lb in enumerate(lens):
+        idx[b, :, :oquest.page_count(lb, 16)] = np.arange(oquest.page_count(lb, 16))
+    sparse = host(da.quest_sparse_decode_attn(dev(case.q), dev(case.k), dev(case.v),
+                                              dev(case.seqlens), dev(idx), budget_tokens=1024,
+                                              page_size=16)).astype(np.float64)
+    dense, _, _ = run_dense(da, case)
+    want = oracle.decode_attention(case.q, case.k, case.v, case.seqlens, case.scale)
+    assert max_err(sparse, want) <= ATOL
+    assert max_err(sparse, dense) <= ATOL
+
+
+def test_sparse_over_paged_cache(da):
+    page_size, lens = 16, [1500, 200]
+    case = workloads.paged_case(520, 2, 32, 8, 128, page_size, 100, lens)
+    kc = oracle.gather_paged(case.k, case.page_table, page_size, case.capacity)
+    vc = oracle.gather_paged(case.v, case.page_table, page_size, case.capacity)
+    meta = oquest.build_metadata(kc, case.seqlens, page_size, 100)
+    idx = oquest.select_pages(oquest.page_scores(case.q, meta, case.seqlens, page_size),
+                              case.seqlens, page_size, 16)
+    out = da.quest_sparse_decode_attn(dev(case.q), dev(case.k), dev(case.v), dev(case.seqlens),
+                                      dev(idx), budget_tokens=256, page_size=page_size,
+                                      page_table=dev(case.page_table))
+    torch.cuda.synchronize()
+    want = oquest.sparse_decode_attention(case.q, kc, vc, case.seqlens, idx, page_size,
+                                          case.scale)
+    assert max_err(host(out), want) <= ATOL
+
+
+def test_quest_pipeline_end_to_end(da):
+    """Metadata -> score/top-K -> sparse attention, all on the GPU, against
+    the oracle running the same steps from the same inputs.  The chosen pages
+    must agree under the near-tie rule; when they agree exactly, the outputs
+    must agree to the attention tolerance."""
+    page_size, budget, lens = 16, 512, [8192, 3000]
+    case = workloads.dense_case(530, 2, 32, 8, 128, 8192, lens, plant_pages=8)
+    meta_dev = run_meta_bulk(da, case, page_size, 512)
+    idx = da.quest_page_score_topk(dev(case.q), meta_dev, dev(case.seqlens), page_size=page_size,
+                                   budget_tokens=budget)
+    out = da.quest_sparse_decode_attn(dev(case.q), dev(case.k), dev(case.v), dev(case.seqlens),
+                                      idx, budget_tokens=budget, page_size=page_size)
+    torch.cuda.synchronize()
+    meta = oquest.build_metadata(case.k, case.seqlens, page_size, 512)
+    scores = oquest.page_scores(case.q, meta, case.seqlens, page_size)
+    want_idx = oquest.select_pages(scores, case.seqlens, page_size, budget // page_size)
+    swaps = check_selection(host(idx), None, want_idx, scores, case.seqlens, page_size,
+                            budget // page_size)
+    if swaps == 0:
+        want = oquest.sparse_decode_attention(case.q, case.k, case.v, case.seqlens, want_idx,
+                                              page_size, case.scale)
+        assert max_err(host(out), want) <= ATOL
