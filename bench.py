@@ -1,0 +1,463 @@
+#!/usr/bin/env python3
+"""Benchmark of folded-GQA decode attention (and Quest) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+Prints ONE JSON line.  A "step" is one pass of the whole hot path over one
+batch of synthetic inputs already resident in HBM:
+
+* exaone30 (default): 30 sequential decode-attention layers shaped like
+  EXAONE 4.0 1.2B (Hq 32, Hkv 8, D 64, fp16 cache [8, 4096, 64] per layer,
+  3000 valid keys, the step's K/V row appended at slot 2999 inside the
+  attention kernel), captured once in a HIP graph and replayed per step.
+* gqa1:        one layer, B 1, Hq 32, Hkv 8, D 64, 4096 keys.
+* paged:       B 64, Hq 32, Hkv 8, D 128, page size 16, lengths U[1024, 32768].
+* quest32k:    Llama2-7B-shaped, B 1, H 32, D 128, L 32768, budget 2048:
+               page score + top-K + sparse attention (dense at the same
+               shape is reported beside it).
+* quest128k:   B 8, Hq 32, Hkv 8, D 128, L 131072, budget 4096: KV append +
+               metadata append, page score + top-K, sparse attention (and
+               dense at the same shape).
+
+Before every timed step a 1 GiB buffer is written (outside the step's events)
+so that neither L2 nor the 256 MiB Infinity Cache holds the inputs.  Step time
+is the median over the K steps of HIP events around the graph replay; the
+dominant kernel's duration comes from events captured between the kernels
+inside the same graph.  `value` is the KV bytes the step must read divided by
+the step time.  The CPU baseline is the fp64 NumPy oracle (1 BLAS thread) on
+a bounded sample of the same workload, timed on the host.
+"""
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TENSORS = ("q", "k", "v", "seqlens", "k_new", "v_new")
+FLUSH_BYTES = 1 << 30
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="exaone30",
+                    choices=["exaone30", "gqa1", "paged", "quest32k", "quest128k"])
+    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=2)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- workloads
+
+
+class Step:
+    """A captured step: graph, the events inside it, byte accounting."""
+
+    def __init__(self, name, config, kv_bytes, algo_bytes, launches, kernel, kernel_bytes,
+                 build_fn, marks):
+        self.name = name
+        self.config = config
+        self.kv_bytes = kv_bytes            # K/V bytes the step must read (the metric)
+        self.algo_bytes = algo_bytes        # every byte the method must move
+        self.launches = launches            # dominant-kernel launches per step
+        self.kernel = kernel                # dominant kernel (name stem)
+        self.kernel_bytes = kernel_bytes    # algorithmic bytes per dominant launch
+        self.build_fn = build_fn            # enqueues one step on the current stream
+        self.marks = marks                  # (label, index of launch) for event pairs
+
+
+def exaone30(da, torch, seed, dev):
+    from decode_attention_folded_amd import workloads
+    layers, hq, hkv, d, cap, L = 30, 32, 8, 64, 4096, 3000
+    data = []
+    for l in range(layers):
+        c = workloads.device_dense(seed * 100 + l, 1, hq, hkv, d, cap, L, dev, with_new=True)
+        c["out"] = torch.empty_like(c["q"])
+        data.append(c)
+    ws = da.Workspace(dev)
+    seqlens = data[0]["seqlens"]
+
+    def one(l):
+        c = data[l]
+        da.gqa_decode_attn(c["q"], c["k"], c["v"], seqlens, k_new=c["k_new"],
+                           v_new=c["v_new"], out=c["out"], workspace=ws)
+
+    kv_layer = 2 * hkv * L * d * 2
+    per_launch = kv_layer + 2 * hkv * d * 2 + 2 * hq * d * 2   # KV + appended row + Q/out
+    cfg = {"workload": "exaone1.2b_30layer_decode_hq32_hkv8_d64_cap4096_len3000_append",
+           "layers": layers, "batch": 1, "num_q_heads": hq, "num_kv_heads": hkv,
+           "head_dim": d, "capacity": cap, "valid_len": L, "dtype_cache": "fp16"}
+    return Step("exaone30", cfg, layers * kv_layer, layers * per_launch, layers,
+                "decode_kernel", per_launch, [lambda l=l: one(l) for l in range(layers)],
+                None), data
+
+
+def gqa1(da, torch, seed, dev):
+    from decode_attention_folded_amd import workloads
+    hq, hkv, d, L = 32, 8, 64, 4096
+    c = workloads.device_dense(seed, 1, hq, hkv, d, L, L, dev)
+    c["out"] = torch.empty_like(c["q"])
+    ws = da.Workspace(dev)
+
+    def one():
+        da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], out=c["out"], workspace=ws)
+
+    kv = 2 * hkv * L * d * 2
+    cfg = {"workload": "gqa_decode_b1_hq32_hkv8_d64_ctx4096", "batch": 1, "num_q_heads": hq,
+           "num_kv_heads": hkv, "head_dim": d, "valid_len": L}
+    return Step("gqa1", cfg, kv, kv + 2 * hq * d * 2, 1, "decode_kernel",
+                kv + 2 * hq * d * 2, [one], None), c
+
+
+def paged(da, torch, seed, dev):
+    import numpy as np
+    from decode_attention_folded_amd import workloads
+    b, hq, hkv, d, s, mp = 64, 32, 8, 128, 16, 2048
+    lens = workloads.draw_seqlens(3, b, 1024, 32768)
+    c = workloads.device_paged(seed, b, hq, hkv, d, s, mp, lens, dev)
+    c["out"] = torch.empty_like(c["q"])
+    ws = da.Workspace(dev)
+
+    def one():
+        da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], page_table=c["page_table"],
+                           page_size=s, out=c["out"], workspace=ws)
+
+    kv = int(2 * hkv * d * 2 * int(np.sum(lens)))
+    per = kv + 2 * b * hq * d * 2 + b * mp * 4
+    cfg = {"workload": "paged_gqa_decode_b64_hq32_hkv8_d128_s16_len1k-32k", "batch": b,
+           "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "page_size": s,
+           "total_tokens": int(np.sum(lens))}
+    return Step("paged", cfg, kv, per, 1, "decode_kernel", per, [one], None), c
+
+
+def quest(da, torch, seed, dev, long_ctx):
+    from decode_attention_folded_amd import workloads
+    if long_ctx:
+        b, hq, hkv, d, L, s, budget, plant = 8, 32, 8, 128, 131072, 16, 4096, 16
+        name = "quest_gqa_b8_hq32_hkv8_d128_L131072_s16_budget4096_append"
+    else:
+        b, hq, hkv, d, L, s, budget, plant = 1, 32, 32, 128, 32768, 16, 2048, 8
+        name = "quest_llama2-7b_b1_h32_d128_L32768_s16_budget2048"
+    c = workloads.device_dense(seed, b, hq, hkv, d, L, L, dev, plant_pages=plant,
+                               plant_page_size=s, with_new=long_ctx)
+    P = L // s
+    meta = torch.zeros((b, hkv, P, 2, d), dtype=torch.float16, device=dev)
+    da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], n_new=L, page_size=s)
+    k_sel = budget // s
+    idx = torch.empty((b, hkv, k_sel), dtype=torch.int32, device=dev)
+    scores = torch.empty((b, hkv, P), dtype=torch.float32, device=dev)
+    out = torch.empty_like(c["q"])
+    dense_out = torch.empty_like(c["q"])
+    ws = da.Workspace(dev)
+    dws = da.Workspace(dev)
+
+    def append():
+        da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], 1, page_size=s,
+                             k_new=c["k_new"], v_new=c["v_new"])
+
+    def select():
+        da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s, budget_tokens=budget,
+                                 page_idx=idx, page_scores=scores)
+
+    def attend():
+        da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx,
+                                    budget_tokens=budget, page_size=s, out=out, workspace=ws)
+
+    def dense():
+        da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], out=dense_out, workspace=dws)
+
+    units = b * hkv
+    meta_bytes = units * P * 2 * d * 2
+    sel_bytes = units * k_sel * s * 2 * d * 2
+    dense_bytes = units * L * 2 * d * 2
+    kv_bytes = meta_bytes + sel_bytes
+    algo = kv_bytes + 2 * units * P * 4 + units * k_sel * 4 + 2 * b * hq * d * 2
+    fns = ([append] if long_ctx else []) + [select, attend]
+    cfg = {"workload": name, "batch": b, "num_q_heads": hq, "num_kv_heads": hkv,
+           "head_dim": d, "seq_len": L, "page_size": s, "budget_tokens": budget,
+           "k_pages": k_sel}
+    st = Step("quest128k" if long_ctx else "quest32k", cfg, kv_bytes, algo, 1,
+              "decode_kernel", sel_bytes + 2 * b * hq * d * 2 + units * k_sel * 4, fns, None)
+    st.dense_fn = dense
+    st.dense_bytes = dense_bytes
+    st.byte_model = {"meta_bytes": meta_bytes, "selected_bytes": sel_bytes,
+                     "dense_bytes": dense_bytes,
+                     "ratio_model": 1.0 / s + budget / L}
+    return st, c
+
+
+# ---------------------------------------------------------------- timing
+
+
+def capture(torch, fns):
+    """Capture the launches of one step into a HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for f in fns:
+                f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, steps, warmup, flush):
+    """Replay the graph warmup + steps times (cache flush before each, outside
+    the events); returns per-step ms."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    step_ms = []
+    for i in range(warmup + steps):
+        if flush is not None:
+            flush.zero_()
+        a.record()
+        g.replay()
+        b.record()
+        if i >= warmup:
+            torch.cuda.synchronize()
+            step_ms.append(a.elapsed_time(b))
+    torch.cuda.synchronize()
+    return step_ms
+
+
+def time_launches(torch, fns, reps, flush):
+    """HIP events around single launches on the launching stream.  The 1 GiB
+    flush enqueued just before keeps the GPU busy while the host enqueues the
+    launch, so the event pair brackets the kernel itself."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    per = [[] for _ in fns]
+    for r in range(reps):
+        for i, f in enumerate(fns):
+            if flush is not None:
+                flush.zero_()
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            per[i].append(a.elapsed_time(b))
+    return per
+
+
+def cpu_baseline(step, data, seed):
+    """The fp64 oracle on a bounded sample of the same workload, 1 BLAS thread."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        return _cpu_baseline(step, data)
+
+
+def _cpu_baseline(step, data):
+    import numpy as np
+    import oracle
+    from oracle import quest as oquest
+    t0 = time.perf_counter()
+    sample = ""
+    bytes_done = 0
+    reps = 0
+    if step.name == "exaone30":
+        host = [{k: v.cpu().numpy() for k, v in c.items() if k in TENSORS} for c in data]
+        t0 = time.perf_counter()
+        while True:
+            for c in host:
+                k2, v2 = oracle.append_kv(c["k"], c["v"], c["seqlens"], c["k_new"], c["v_new"])
+                oracle.decode_attention(c["q"], k2, v2, c["seqlens"], 1 / 8.0)
+            reps += 1
+            bytes_done += step.kv_bytes
+            if time.perf_counter() - t0 > 10.0 or reps >= 3:
+                break
+        sample = f"{reps} full 30-layer step(s) (append + repeat_kv attention, fp64)"
+    elif step.name in ("gqa1",):
+        c = {k: v.cpu().numpy() for k, v in data.items() if k in TENSORS}
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 10.0 and reps < 20:
+            oracle.decode_attention(c["q"], c["k"], c["v"], c["seqlens"], 1 / 8.0)
+            reps += 1
+            bytes_done += step.kv_bytes
+        sample = f"{reps} full step(s)"
+    elif step.name == "paged":
+        # a few sequences of the batch
+        lens = data["seqlens_host"]
+        table = data["page_table_host"]
+        t0 = None
+        for b in range(4):
+            n = (int(lens[b]) + 15) // 16
+            pages = table[b, :n]
+            k = data["k"][torch_index(pages)].cpu().numpy()
+            v = data["v"][torch_index(pages)].cpu().numpy()
+            q = data["q"][b:b + 1].cpu().numpy()
+            kc = k.transpose(1, 0, 2, 3).reshape(1, k.shape[1], n * 16, k.shape[3])
+            vc = v.transpose(1, 0, 2, 3).reshape(1, v.shape[1], n * 16, v.shape[3])
+            s0 = time.perf_counter()
+            oracle.decode_attention(q, kc, vc, [int(lens[b])], 1 / math.sqrt(128))
+            t0 = (t0 or 0.0) + time.perf_counter() - s0
+            bytes_done += 2 * 8 * int(lens[b]) * 128 * 2
+        sample = "4 of the 64 sequences"
+        return _baseline(bytes_done, t0, sample)
+    else:
+        # Quest: one or two (b, kv) units through every step of the method
+        b_units = [(0, 0), (0, 1)]
+        c = data
+        S = step.config["page_size"]
+        budget = step.config["budget_tokens"]
+        L = step.config["seq_len"]
+        G = step.config["num_q_heads"] // step.config["num_kv_heads"]
+        elapsed = 0.0
+        for (b, kv) in b_units:
+            q = c["q"][b:b + 1, kv * G:(kv + 1) * G].cpu().numpy()
+            k = c["k"][b:b + 1, kv:kv + 1].cpu().numpy()
+            v = c["v"][b:b + 1, kv:kv + 1].cpu().numpy()
+            lens = np.array([L], np.int32)
+            s0 = time.perf_counter()
+            meta = oquest.build_metadata(k, lens, S, L // S)
+            u = oquest.page_scores(q, meta, lens, S)
+            idx = oquest.select_pages(u, lens, S, budget // S)
+            oquest.sparse_decode_attention(q, k, v, lens, idx, S, 1 / math.sqrt(128))
+            elapsed += time.perf_counter() - s0
+            bytes_done += step.kv_bytes // (step.config["batch"] * step.config["num_kv_heads"])
+        sample = f"{len(b_units)} (b, kv) units, metadata build + score + top-K + sparse attention"
+        return _baseline(bytes_done, elapsed, sample)
+    elapsed = time.perf_counter() - t0
+    return _baseline(bytes_done, elapsed, sample)
+
+
+def torch_index(pages):
+    import torch
+    return torch.from_numpy(pages.astype("int64"))
+
+
+def _baseline(bytes_done, elapsed, sample):
+    return {"value": round(bytes_done / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": sample, "seconds": round(elapsed, 3)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "no multi-GPU path exists", file=sys.stderr)
+        return 2
+    import torch
+    import decode_attention_folded_amd as da
+    da.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    maker = {"exaone30": exaone30, "gqa1": gqa1, "paged": paged,
+             "quest32k": lambda *a: quest(*a, long_ctx=False),
+             "quest128k": lambda *a: quest(*a, long_ctx=True)}[args.workload]
+    step, data = maker(da, torch, args.seed, dev)
+    flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    # eager warm-up allocates every workspace before capture
+    for f in step.build_fn:
+        f()
+    if hasattr(step, "dense_fn"):
+        step.dense_fn()
+    torch.cuda.synchronize()
+
+    g = capture(torch, step.build_fn)
+
+    # timed region: K graph-replayed steps, then the step's launches one at a
+    # time under HIP events (the dominant kernel's duration)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    step_ms = time_graph(torch, g, args.steps, args.warmup, flush)
+    reps = max(1, args.steps // len(step.build_fn)) if len(step.build_fn) > 1 else args.steps
+    launch_ms = time_launches(torch, step.build_fn, reps, flush)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+
+    ms = statistics.median(step_ms)
+    gbs = step.kv_bytes / (ms * 1e-3) / 1e9
+    # dominant kernel: the attention launches (every launch of the dense
+    # workloads; the sparse-attention launch of a Quest step)
+    if step.name.startswith("quest"):
+        per = launch_ms[-1]
+    else:
+        per = [x for col in launch_ms for x in col]
+    kern_ms = statistics.median(per)
+    kern_src = "hip events around single launches after a cache flush (median)"
+    achieved = step.kernel_bytes / (kern_ms * 1e-3) / 1e9
+
+    extra = {
+        "us_per_step": round(ms * 1e3, 3),
+        "us_p10": round(sorted(step_ms)[len(step_ms) // 10] * 1e3, 3),
+        "us_p90": round(sorted(step_ms)[(len(step_ms) * 9) // 10] * 1e3, 3),
+        "kv_bytes_per_step": step.kv_bytes,
+        "algorithmic_bytes_per_step": step.algo_bytes,
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "cache_flush_between_steps": flush is not None,
+        "graph": "step replayed from one captured HIP graph",
+        "kernel_time_source": kern_src,
+        "timed_wall_s": round(t_wall, 3),
+    }
+    extra["sum_of_launches_us"] = round(sum(statistics.median(c) for c in launch_ms) * 1e3, 3)
+    if hasattr(step, "dense_fn"):
+        dense_ms = statistics.median(time_launches(torch, [step.dense_fn],
+                                                   max(10, args.steps // 2), flush)[0])
+        extra["dense_same_shape_us"] = round(dense_ms * 1e3, 3)
+        extra["dense_same_shape_gbs"] = round(step.dense_bytes / (dense_ms * 1e-3) / 1e9, 1)
+        extra["dense_same_shape_pct_peak"] = round(
+            100 * step.dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+        extra["quest_over_dense_time"] = round(ms / dense_ms, 4)
+        extra["byte_model"] = step.byte_model
+        names = (["meta_append"] if step.name == "quest128k" else []) + \
+            ["score_topk", "sparse_attention"]
+        extra["stage_us"] = {n: round(statistics.median(col) * 1e3, 3)
+                             for n, col in zip(names, launch_ms)}
+
+    # reference copy of known size (scales the FETCH/WRITE counters in the
+    # counter runs); not part of the timed region
+    src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+    line = {
+        "metric": "decode-attn KV GB/s (% HBM peak) + us/step",
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in, f32 accumulate",
+        "data": "synthetic N(0,1) fp16, seeded",
+        "config": step.config,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 3),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": step.kernel,
+            "kernel_us": round(kern_ms * 1e3, 3),
+            "bytes_per_launch": step.kernel_bytes,
+        },
+    }
+    line.update(extra)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(step, data, args.seed)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -170,9 +170,9 @@ def _out_like(q, out):
 
 
 class Workspace:
-    """A zero-initialised device buffer that grows on demand.  The library's
-    split counters return to zero after every completed call, so one
-    workspace serves any number of calls on one stream."""
+    """A device scratch buffer that grows on demand; it holds only per-call
+    partial results, so one workspace serves any number of calls issued in
+    order on one stream."""
 
     def __init__(self, device=None):
         self.device = device
@@ -189,9 +189,8 @@ _DEFAULT_WS = {}
 
 
 def _workspace(ws, device, kind="attn"):
-    # The attention calls share one default workspace (their counters are
-    # zero again after every call); page scores get their own so they never
-    # overwrite those counters.
+    # The attention calls share one default workspace; page scores get their
+    # own, so a score buffer is never overwritten by a later attention call.
     if ws is None:
         key = (kind, device.type, device.index)
         ws = _DEFAULT_WS.setdefault(key, Workspace(device))

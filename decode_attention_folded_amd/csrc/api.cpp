@@ -8,6 +8,8 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "../../include/decode_attn.h"
 #include "kernels.h"
@@ -92,14 +94,15 @@ da::SplitPlan plan_splits(const Shape& s, int max_keys, int num_splits) {
 }
 
 struct WsLayout {
-  size_t counters, ml, o, total;
+  size_t ml, o, total;
 };
 
+// Workspace: per (b, kv, split) partial softmax state (m, l) and
+// unnormalised output o, all fp32.
 WsLayout ws_layout(const Shape& s, const da::SplitPlan& p) {
   const size_t units = (size_t)s.batch * s.hkv;
   WsLayout w;
-  w.counters = 0;
-  w.ml = align256(units * sizeof(uint32_t));
+  w.ml = 0;
   w.o = w.ml + align256(units * p.max_splits * s.group * 2 * sizeof(float));
   w.total = w.o + units * p.max_splits * s.group * s.d * sizeof(float);
   if (w.total == 0) w.total = 256;
@@ -113,6 +116,16 @@ int max_stream_keys(const Shape& s, int budget_tokens) {
   if (budget_tokens <= 0) return s.capacity;
   const int64_t all_pages = ((int64_t)s.capacity + s.page_size - 1) / s.page_size * s.page_size;
   return (int)(budget_tokens < all_pages ? budget_tokens : all_pages);
+}
+
+// q.k on the matrix cores (MFMA) unless DECODE_ATTN_QK=valu selects the
+// v_dot2 path; read once.
+bool qk_on_matrix_cores() {
+  static const bool mfma = [] {
+    const char* v = getenv("DECODE_ATTN_QK");
+    return !(v != nullptr && strcmp(v, "valu") == 0);
+  }();
+  return mfma;
 }
 
 int check_budget(const Shape& s, int budget_tokens) {
@@ -160,7 +173,6 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
   a.k_new = k_new;
   a.v_new = v_new;
   a.out = out;
-  a.counters = reinterpret_cast<uint32_t*>(ws + w.counters);
   a.part_ml = reinterpret_cast<float*>(ws + w.ml);
   a.part_o = reinterpret_cast<float*>(ws + w.o);
   a.batch = s.batch;
@@ -176,6 +188,7 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
   a.tiles_per_split = plan.tiles_per_split;
   a.max_splits = plan.max_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.qk_mfma = qk_on_matrix_cores() ? 1 : 0;
   return da::launch_decode(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
 }
 

@@ -9,31 +9,38 @@
 // loop over the tokens of the chosen pages only.
 //
 // Work decomposition (flash-decode): grid = (splits, Hkv, B).  A workgroup of
-// 4 waves owns a contiguous chunk of `tiles_per_split` key tiles of one
-// (b, kv) unit; its waves take the chunk's tiles round robin.
+// 4 waves owns a contiguous chunk of `tiles_per_split` 16-key tiles of one
+// (b, kv) unit; its waves take the chunk's tiles round robin.  Each split
+// writes a partial (running max m, sum l, unnormalised o) and a second, small
+// kernel merges the splits (log-sum-exp).  Merging in its own launch avoids
+// device-scope cache write-back/invalidate fences, which on a multi-XCD part
+// cost far more than one extra launch.
 //
-// Lane layout inside a wave (W lanes per key, KT = 64 / W keys per tile):
-//   lane = c * KT + r; r = key slot in the tile, c = channel group.
-//   Lane (r, c) loads 16-byte chunks W*jj + c (jj < D / (8W)) of key r's K and
-//   V rows, so one load instruction covers W*16 contiguous bytes of each of
-//   KT keys.  The partial q.k over the lane's channels (v_dot2_f32_f16) is
-//   summed over the W lanes of the key with cross-row exchanges; after that
-//   all W lanes hold the same score.
-//   Each lane keeps its own online-softmax state (running max m, sum l and
-//   the fp32 output accumulator for its channels) over the keys that pass
-//   through its slot r; the KT slot states are merged once at the end of the
-//   chunk (log-sum-exp), then the 4 waves are merged through LDS.
-//   Rescaling is lazy: the running max only moves when a score exceeds it by
-//   more than 2^8 (in exp2 units), so steady-state tiles do no rescale work.
+// Lane layout of one 16-key tile (lane = 0..63):
+//   K: lane holds key (lane % 16), 16-byte channel chunks 4*j + lane/16,
+//      j < D/32 -- the B-operand layout of v_mfma_f32_16x16x16f16 (k =
+//      channel, n = key), so a tile feeds the matrix core as loaded.
+//   V: lane holds keys (lane % 8) and (lane % 8) + 8, chunks 8*h + lane/8,
+//      h < D/64: each load instruction covers 128 contiguous bytes of each
+//      of 8 keys, and a lane accumulates only D/8 channels per query row.
+// Scores: with QK_MFMA the G query rows are replicated over the 16 rows of
+// the MFMA A operand, so every lane receives all G scores of its K key; the
+// VALU variant (v_dot2_f32_f16 over the lane's channels, then a sum over the
+// 4 lanes of the key) gives the same placement.  One DPP exchange (lane ^ 8)
+// hands each lane the scores of its two V keys.
+// Each lane keeps its own online-softmax state (m, l, fp32 accumulators) over
+// the keys that pass through its slots; the 8 slot states of a channel group
+// are merged at the end of the chunk, then the 4 waves through LDS.
+// Rescaling is lazy: the running max only moves when a score exceeds it by
+// more than 2^8 (exp2 units), so steady-state tiles skip the rescale.
+// Tiles are loaded into a ring of NS register stages, so NS - 1 tiles are in
+// flight while one is computed.
 //
-// Split combine: each workgroup writes its (m, l, o) partial; the last
-// workgroup of a unit to finish (atomic counter, reset by that workgroup)
-// merges all partials in split order and writes the fp16 output.  No
-// floating-point atomics: results are bitwise reproducible.
-//
-// Keys at or past the valid length are never loaded from their slots: their
-// loads are redirected to a valid row of the same unit and their scores forced
-// to -inf, so whatever the cache holds there (even NaN) cannot leak in.
+// Keys at or past the valid length are never loaded from their own slots:
+// their loads are redirected to a valid row of the same sequence and their
+// scores forced to -inf, so whatever the cache holds there (even NaN) cannot
+// leak into the result.  No floating-point atomics: results are bitwise
+// reproducible.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -45,50 +52,78 @@
 namespace da {
 namespace {
 
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
+constexpr int kTileKeys = 16;
 constexpr int kMaxTilesPerSplit = 128;
-constexpr int kMinKeysPerTile = 8;
 constexpr int kMinPageSize = 8;
 // pages (or chosen-page entries) one chunk can touch
-constexpr int kMaxChunkPages = kMaxTilesPerSplit * 16 / kMinPageSize + 2;
+constexpr int kMaxChunkPages = kMaxTilesPerSplit * kTileKeys / kMinPageSize + 2;
 constexpr float kRescaleThreshold = 8.0f;
 constexpr float kNegBig = -1.0e30f;
+constexpr int kStages = 3;
 
-template <int D, int G>
-struct Lanes {
-  static constexpr int W = (D == 128 && G == 8) ? 8 : 4;  // lanes per key
-  static constexpr int KT = kWave / W;                     // keys per tile
-  static constexpr int NC = D / (8 * W);                   // 16-byte chunks per lane
-  static constexpr int NV = NC * 8;                        // channels per lane
+// Keys in the (b, kv) key stream and the number of splits that cover it;
+// shared by the attention and the merge kernel.
+struct StreamInfo {
+  int L;        // valid length after clamping
+  int n_keys;   // keys in the stream (dense: L; chosen pages: nsel * S)
+  int nsplit;   // splits with at least one key
 };
 
-template <int NC>
-struct TileRegs {
-  f16x8 k[NC];
-  f16x8 v[NC];
-  bool valid;
+__device__ __forceinline__ StreamInfo stream_info(const AttnLaunch& a, int b, bool sparse) {
+  StreamInfo si;
+  const int L = a.seqlens[b];
+  si.L = L < 0 ? 0 : (L > a.capacity ? a.capacity : L);
+  si.n_keys = si.L;
+  if (sparse) {
+    const int pages = (si.L + (1 << a.page_shift) - 1) >> a.page_shift;
+    const int nsel = pages < a.num_sel ? pages : a.num_sel;
+    si.n_keys = nsel << a.page_shift;
+  }
+  const int n_tiles = (si.n_keys + kTileKeys - 1) / kTileKeys;
+  si.nsplit = (n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  return si;
+}
+
+template <int D>
+struct Layout {
+  static constexpr int NCK = D / 32;   // K chunks per lane per tile
+  static constexpr int NCV = D / 64;   // V chunks per lane per key (2 keys)
+  static constexpr int NV = NCV * 8;   // channels per lane
 };
 
-template <int D, int G, bool PAGED, bool SPARSE>
+template <int D>
+struct Stage {
+  f16x8 k[Layout<D>::NCK];
+  f16x8 v0[Layout<D>::NCV];  // key (lane % 8)
+  f16x8 v1[Layout<D>::NCV];  // key (lane % 8) + 8
+  bool kvalid;               // the K key of this lane
+};
+
+template <int D, int G, bool PAGED, bool SPARSE, bool QK_MFMA>
 __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
-  using LN = Lanes<D, G>;
-  constexpr int W = LN::W;
-  constexpr int KT = LN::KT;
-  constexpr int NC = LN::NC;
-  constexpr int NV = LN::NV;
+  constexpr int NCK = Layout<D>::NCK;
+  constexpr int NCV = Layout<D>::NCV;
+  constexpr int NV = Layout<D>::NV;
+  constexpr int GC = (G + 3) / 4;  // MFMA chains (4 query rows each)
+  constexpr int NS = kStages;
 
   __shared__ float s_o[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ int32_t s_page[(PAGED || SPARSE) ? kMaxChunkPages : 1];
   __shared__ int32_t s_phys[(PAGED && SPARSE) ? kMaxChunkPages : 1];
-  __shared__ int s_last;
 
   const int lane = lane_in_wave();
   const int wave = threadIdx.x / kWave;
-  const int r = lane % KT;
-  const int c = lane / KT;
+  const int rk = lane & 15;        // K key slot
+  const int ck = lane >> 4;        // K chunk group (0..3)
+  const int rv = lane & 7;         // V key slots rv, rv + 8
+  const int cv = lane >> 3;        // V chunk group (0..7)
+  const bool upper = (lane & 8) != 0;
   const int split = blockIdx.x;
   const int kv = blockIdx.y;
   const int b = blockIdx.z;
@@ -97,16 +132,11 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   const int shift = a.page_shift;
   const int page_mask = (1 << shift) - 1;
 
-  int L = a.seqlens[b];
-  L = L < 0 ? 0 : (L > a.capacity ? a.capacity : L);
-  int n_keys = L;
+  const StreamInfo si = stream_info(a, b, SPARSE);
+  const int L = si.L;
+  const int n_keys = si.n_keys;
+  const int nsplit = si.nsplit;
   const int n_pages_L = (L + page_mask) >> shift;
-  if constexpr (SPARSE) {
-    const int nsel = n_pages_L < a.num_sel ? n_pages_L : a.num_sel;
-    n_keys = nsel << shift;
-  }
-  const int n_tiles = (n_keys + KT - 1) / KT;
-  const int nsplit = (n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;
   f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;  // rows h = G*kv + g of batch b
 
   if (split >= nsplit) {
@@ -116,22 +146,22 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
     return;
   }
 
+  const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
   const int tile_begin = split * a.tiles_per_split;
   const int tile_end = min(tile_begin + a.tiles_per_split, n_tiles);
-  const int key_begin = tile_begin * KT;
-  const int key_last = min(tile_end * KT, n_keys) - 1;
+  const int key_begin = tile_begin * kTileKeys;
+  const int key_last = min(tile_end * kTileKeys, n_keys) - 1;
   const int page0 = key_begin >> shift;
 
   // Page lists of this chunk into LDS: the physical page of each logical page
   // (paged cache) and/or the chosen logical pages (selected-page stream).
+  // Entries that do not name an existing page become -1.
   if constexpr (PAGED || SPARSE) {
     const int npg = (key_last >> shift) - page0 + 1;
     for (int i = threadIdx.x; i < npg; i += kThreads) {
       int logical = page0 + i;
-      if constexpr (SPARSE) logical = a.page_idx[unit * a.num_sel + page0 + i];
       if constexpr (SPARSE) {
-        // a chosen page must exist: 0 <= page < ceil(L / S); anything else
-        // is masked (-1) so that no address is formed from it
+        logical = a.page_idx[unit * a.num_sel + page0 + i];
         if (logical < 0 || logical >= n_pages_L) logical = -1;
       }
       int entry = logical;
@@ -171,14 +201,28 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   const f16* knew_row = has_new ? reinterpret_cast<const f16*>(a.k_new) + unit * D : nullptr;
   const f16* vnew_row = has_new ? reinterpret_cast<const f16*>(a.v_new) + unit * D : nullptr;
 
-  // Folded queries: G rows of this KV head, the lane's channels only.
+  // Folded queries of this KV head.
   const f16* qb = reinterpret_cast<const f16*>(a.q) + unit * G * D;
-  f16x8 qr[G][NC];
+  // MFMA A operand: row i of chain c is query g = (4c + i % 4) mod G; the lane
+  // holds row lane % 16 over the k-slots of chunk 4j + ck.
+  f16x8 qa[QK_MFMA ? GC : 1][QK_MFMA ? NCK : 1];
+  // VALU operand: all G rows over the lane's K channels.
+  f16x8 qv[QK_MFMA ? 1 : G][QK_MFMA ? 1 : NCK];
+  if constexpr (QK_MFMA) {
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+    for (int cch = 0; cch < GC; ++cch) {
+      const int g = (4 * cch + (rk & 3)) % G;
 #pragma unroll
-    for (int jj = 0; jj < NC; ++jj)
-      qr[g][jj] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (W * jj + c));
+      for (int j = 0; j < NCK; ++j)
+        qa[cch][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < NCK; ++j)
+        qv[g][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
+  }
 
   float m[G], l[G], acc[G][NV];
 #pragma unroll
@@ -189,14 +233,38 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
     for (int x = 0; x < NV; ++x) acc[g][x] = 0.0f;
   }
 
-  auto load_tile = [&](int tile, TileRegs<NC>& T) {
-    const int j = tile * KT + r;  // position in this unit's key stream
-    int t = j;                    // token position in the sequence
-    bool valid = j < n_keys;
+  // Append: the new row goes to slot L - 1 of the cache.  Only the workgroup
+  // whose chunk holds that slot writes it, and its own loads of that key are
+  // redirected to k_new/v_new, so no other read of the slot can race.
+  if (has_new && !SPARSE && key_begin <= L - 1 && L - 1 <= key_last) {
+    int64_t off;
+    if constexpr (PAGED) {
+      int phys = a.page_table[(int64_t)b * a.max_pages + ((L - 1) >> shift)];
+      off = (phys >= 0 && phys < a.num_pages)
+                ? (((int64_t)phys * hkv + kv) << shift) * D + (int64_t)((L - 1) & page_mask) * D
+                : -1;
+    } else {
+      off = (unit * a.cache_stride + (L - 1)) * D;
+    }
+    if (off >= 0 && threadIdx.x < 2 * (D / 8)) {
+      const int c16 = threadIdx.x % (D / 8);
+      const f16* src = (threadIdx.x < D / 8 ? knew_row : vnew_row) + 8 * c16;
+      f16* dst = reinterpret_cast<f16*>(threadIdx.x < D / 8 ? a.k : a.v) + off + 8 * c16;
+      *reinterpret_cast<f16x8*>(dst) = *reinterpret_cast<const f16x8*>(src);
+    }
+  }
+
+  // Element offset of stream position j (or the safe row), its validity and
+  // its token index.  Positions outside this chunk (live = false) resolve to
+  // the safe row: the stage ring issues its loads unconditionally so that the
+  // compiler's wait counts stay exact, and such loads only touch that row.
+  auto resolve = [&](int j, bool live, bool& valid, int& t) -> int64_t {
+    t = j;
+    valid = live && j < n_keys;
     int64_t off;
     if constexpr (SPARSE) {
-      const int li = (j >> shift) - page0;
-      const int logical = valid ? s_page[li] : 0;
+      const int li = valid ? (j >> shift) - page0 : 0;  // in range of the LDS list
+      const int logical = valid ? s_page[li] : -1;
       t = (logical << shift) + (j & page_mask);
       valid = valid && logical >= 0 && t < L;
       if constexpr (PAGED) {
@@ -207,57 +275,88 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
         off = (unit * a.cache_stride + t) * D;
       }
     } else if constexpr (PAGED) {
-      const int phys = valid ? s_page[(j >> shift) - page0] : -1;
+      const int phys = valid ? s_page[valid ? (j >> shift) - page0 : 0] : -1;
       valid = valid && phys >= 0;
       off = (((int64_t)phys * hkv + kv) << shift) * D + (int64_t)(t & page_mask) * D;
     } else {
       off = (unit * a.cache_stride + t) * D;
     }
-    if (!valid) off = safe_off;
-    T.valid = valid;
-    const bool is_new = has_new && valid && t == L - 1;
-    const f16* kp = kc + off;
-    const f16* vp = vc + off;
-    if (is_new) {
-      kp = knew_row;
-      vp = vnew_row;
-    }
+    return valid ? off : safe_off;
+  };
+
+  // Loads of one tile; no branches, so every stage issues the same number of
+  // loads and the wait for a stage leaves the later stages in flight.
+  auto load_stage = [&](int tile, Stage<D>& st) {
+    const bool live = tile < tile_end;
+    const int j0 = tile * kTileKeys;
+    bool vk, v0, v1;
+    int tk, t0, t1;
+    const int64_t ok = resolve(j0 + rk, live, vk, tk);
+    const int64_t o0 = resolve(j0 + rv, live, v0, t0);
+    const int64_t o1 = resolve(j0 + rv + 8, live, v1, t1);
+    st.kvalid = vk;
+    // The appended key reads k_new/v_new; with an append, masked keys read it
+    // too (the slot being written may not hold finite data yet).
+    const f16* kp = (has_new && (!vk || tk == L - 1)) ? knew_row : kc + ok;
+    const f16* vp0 = (has_new && (!v0 || t0 == L - 1)) ? vnew_row : vc + o0;
+    const f16* vp1 = (has_new && (!v1 || t1 == L - 1)) ? vnew_row : vc + o1;
 #pragma unroll
-    for (int jj = 0; jj < NC; ++jj) {
-      T.k[jj] = *reinterpret_cast<const f16x8*>(kp + 8 * (W * jj + c));
-      T.v[jj] = *reinterpret_cast<const f16x8*>(vp + 8 * (W * jj + c));
-    }
-    if (is_new) {  // append: the new row goes to slot L - 1 of the cache
-      f16* kd = reinterpret_cast<f16*>(a.k) + off;
-      f16* vd = reinterpret_cast<f16*>(a.v) + off;
+    for (int j = 0; j < NCK; ++j)
+      st.k[j] = *reinterpret_cast<const f16x8*>(kp + 8 * (4 * j + ck));
 #pragma unroll
-      for (int jj = 0; jj < NC; ++jj) {
-        *reinterpret_cast<f16x8*>(kd + 8 * (W * jj + c)) = T.k[jj];
-        *reinterpret_cast<f16x8*>(vd + 8 * (W * jj + c)) = T.v[jj];
-      }
+    for (int h = 0; h < NCV; ++h) {
+      st.v0[h] = *reinterpret_cast<const f16x8*>(vp0 + 8 * (8 * h + cv));
+      st.v1[h] = *reinterpret_cast<const f16x8*>(vp1 + 8 * (8 * h + cv));
     }
   };
 
-  auto compute_tile = [&](const TileRegs<NC>& T) {
-    float s[G];
+  auto compute_stage = [&](const Stage<D>& st) {
+    // scores of this lane's K key, all G rows
+    float sk[G];
+    if constexpr (QK_MFMA) {
+#pragma unroll
+      for (int cch = 0; cch < GC; ++cch) {
+        f32x4 d4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < NCK; ++j) {
+          const f16x4 blo = {st.k[j][0], st.k[j][1], st.k[j][2], st.k[j][3]};
+          const f16x4 bhi = {st.k[j][4], st.k[j][5], st.k[j][6], st.k[j][7]};
+          const f16x4 alo = {qa[cch][j][0], qa[cch][j][1], qa[cch][j][2], qa[cch][j][3]};
+          const f16x4 ahi = {qa[cch][j][4], qa[cch][j][5], qa[cch][j][6], qa[cch][j][7]};
+          d4 = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, d4, 0, 0, 0);
+          d4 = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, d4, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * cch + r < G) sk[4 * cch + r] = d4[r];
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float x = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NCK; ++j) x = dot8(qv[g][j], st.k[j], x);
+        x += lane_xor<16>(x);
+        x += lane_xor<32>(x);
+        sk[g] = x;
+      }
+    }
+    // scores of the two V keys of this lane: keys (lane % 8) and + 8
+    float sa[G], sb[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float x = 0.0f;
-#pragma unroll
-      for (int jj = 0; jj < NC; ++jj) x = dot8(qr[g][jj], T.k[jj], x);
-      // sum over the W lanes of this key
-      if constexpr (W == 8) x += lane_xor<8>(x);
-      x += lane_xor<16>(x);
-      x += lane_xor<32>(x);
-      s[g] = T.valid ? x * a.scale_log2 : -INFINITY;
+      const float mine = st.kvalid ? sk[g] * a.scale_log2 : -INFINITY;
+      const float other = lane_xor<8>(mine);
+      sa[g] = upper ? other : mine;
+      sb[g] = upper ? mine : other;
     }
     bool need = false;
 #pragma unroll
-    for (int g = 0; g < G; ++g) need |= s[g] > m[g] + kRescaleThreshold;
+    for (int g = 0; g < G; ++g) need |= fmaxf(sa[g], sb[g]) > m[g] + kRescaleThreshold;
     if (need) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float mn = fmaxf(m[g], s[g]);
+        const float mn = fmaxf(m[g], fmaxf(sa[g], sb[g]));
         const float f = fast_exp2(m[g] - mn);
         l[g] *= f;
 #pragma unroll
@@ -267,59 +366,58 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float p = fast_exp2(s[g] - m[g]);
-      l[g] += p;
+      const float pa = fast_exp2(sa[g] - m[g]);
+      const float pb = fast_exp2(sb[g] - m[g]);
+      l[g] += pa + pb;
 #pragma unroll
-      for (int jj = 0; jj < NC; ++jj)
+      for (int h = 0; h < NCV; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          acc[g][jj * 8 + e] = fmaf(p, (float)T.v[jj][e], acc[g][jj * 8 + e]);
+        for (int e = 0; e < 8; ++e) {
+          const float x = fmaf(pa, (float)st.v0[h][e], acc[g][h * 8 + e]);
+          acc[g][h * 8 + e] = fmaf(pb, (float)st.v1[h][e], x);
+        }
     }
   };
 
-  // Two register buffers: the next tile's loads are in flight while the
-  // current tile is computed.
+  // Ring of NS register stages: stage s holds the wave's tiles first + s*4,
+  // first + (s + NS)*4, ... (4 = waves per workgroup, the wave's stride).
   {
-    TileRegs<NC> A, B;
-    int tile = tile_begin + wave;
-    if (tile < tile_end) {
-      load_tile(tile, A);
-      while (true) {
-        const int t1 = tile + kWaves;
-        if (t1 < tile_end) load_tile(t1, B);
-        compute_tile(A);
-        if (t1 >= tile_end) break;
-        const int t2 = t1 + kWaves;
-        if (t2 < tile_end) load_tile(t2, A);
-        compute_tile(B);
-        if (t2 >= tile_end) break;
-        tile = t2;
+    Stage<D> st[NS];
+    const int first = tile_begin + wave;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) load_stage(first + s * kWaves, st[s]);
+    for (int base = first; base < tile_end; base += NS * kWaves) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int t = base + s * kWaves;
+        if (t < tile_end) compute_stage(st[s]);
+        load_stage(t + NS * kWaves, st[s]);
       }
     }
   }
 
-  // Merge the KT key slots of each channel group (log-sum-exp).
+  // Merge the 8 key slots of each V channel group (log-sum-exp).
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float M = group_max<KT>(m[g]);
+    const float M = group_max<8>(m[g]);
     const float f = fast_exp2(m[g] - M);
-    l[g] = group_sum<KT>(l[g] * f);
+    l[g] = group_sum<8>(l[g] * f);
 #pragma unroll
-    for (int x = 0; x < NV; ++x) acc[g][x] = group_sum<KT>(acc[g][x] * f);
+    for (int x = 0; x < NV; ++x) acc[g][x] = group_sum<8>(acc[g][x] * f);
     m[g] = M;
   }
-  if (r == 0) {
+  if (rv == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int jj = 0; jj < NC; ++jj) {
-        float* dst = &s_o[wave][g][8 * (W * jj + c)];
+      for (int h = 0; h < NCV; ++h) {
+        float* dst = &s_o[wave][g][8 * (8 * h + cv)];
         *reinterpret_cast<f32x4*>(dst) =
-            f32x4{acc[g][jj * 8 + 0], acc[g][jj * 8 + 1], acc[g][jj * 8 + 2], acc[g][jj * 8 + 3]};
+            f32x4{acc[g][h * 8 + 0], acc[g][h * 8 + 1], acc[g][h * 8 + 2], acc[g][h * 8 + 3]};
         *reinterpret_cast<f32x4*>(dst + 4) =
-            f32x4{acc[g][jj * 8 + 4], acc[g][jj * 8 + 5], acc[g][jj * 8 + 6], acc[g][jj * 8 + 7]};
+            f32x4{acc[g][h * 8 + 4], acc[g][h * 8 + 5], acc[g][h * 8 + 6], acc[g][h * 8 + 7]};
       }
-      if (c == 0) {
+      if (cv == 0) {
         s_m[wave][g] = m[g];
         s_l[wave][g] = l[g];
       }
@@ -327,7 +425,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   }
   __syncthreads();
 
-  // Merge the waves of this workgroup.
+  // Merge the waves of this workgroup; write the output (single split) or
+  // this split's partial.
   float* part_o = a.part_o + (unit * a.max_splits + split) * G * D;
   float* part_ml = a.part_ml + (unit * a.max_splits + split) * G * 2;
   for (int i = threadIdx.x; i < G * D; i += kThreads) {
@@ -353,40 +452,65 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
       }
     }
   }
-  if (nsplit == 1) return;
+}
 
-  // Publish this split; the last one of the unit combines all of them.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&a.counters[unit], 1u);
-    s_last = prev == (unsigned)(nsplit - 1);
+// Merge the split partials of every (b, kv) unit that has more than one split:
+// O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, in split order.
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads) merge_kernel(AttnLaunch a, bool sparse) {
+  __shared__ float s_max[G];
+  __shared__ float s_inv[G];
+  const int kv = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t unit = (int64_t)b * a.num_kv_heads + kv;
+  const StreamInfo si = stream_info(a, b, sparse);
+  const int nsplit = si.nsplit;
+  if (nsplit <= 1) return;  // the attention kernel wrote the output
+  const float* ml = a.part_ml + unit * a.max_splits * G * 2;
+  const float* po = a.part_o + unit * a.max_splits * G * D;
+  f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_in_wave();
+  for (int g = wave; g < G; g += kWaves) {
+    float M = kNegBig;
+    for (int sp = lane; sp < nsplit; sp += kWave) M = fmaxf(M, ml[(sp * G + g) * 2]);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, kWave));
+    float lsum = 0.0f;
+    for (int sp = lane; sp < nsplit; sp += kWave)
+      lsum += fast_exp2(ml[(sp * G + g) * 2] - M) * ml[(sp * G + g) * 2 + 1];
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) lsum += __shfl_xor(lsum, d, kWave);
+    if (lane == 0) {
+      s_max[g] = M;
+      s_inv[g] = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    }
   }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  const float* all_o = a.part_o + unit * a.max_splits * G * D;
-  const float* all_ml = a.part_ml + unit * a.max_splits * G * 2;
   for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const int g = i / D;
-    float M = kNegBig;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, all_ml[(sp * G + g) * 2]);
-    float o = 0.0f, lsum = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float f = fast_exp2(all_ml[(sp * G + g) * 2] - M);
-      o += f * all_o[sp * G * D + i];
-      lsum += f * all_ml[(sp * G + g) * 2 + 1];
-    }
-    out[i] = (f16)(lsum > 0.0f ? o / lsum : 0.0f);
+    const float M = s_max[g];
+    float o = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp)
+      o = fmaf(fast_exp2(ml[(sp * G + g) * 2] - M), po[sp * G * D + i], o);
+    out[i] = (f16)(o * s_inv[g]);
   }
-  if (threadIdx.x == 0) a.counters[unit] = 0u;
 }
 
 template <int D, int G, bool PAGED, bool SPARSE>
 int launch_one(const AttnLaunch& a, hipStream_t stream) {
   dim3 grid(a.max_splits, a.num_kv_heads, a.batch);
-  hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+  if (a.qk_mfma) {
+    hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, true>), grid, dim3(kThreads), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, false>), grid, dim3(kThreads), 0,
+                       stream, a);
+  }
+  const int err = (int)hipGetLastError();
+  if (err != 0 || a.max_splits <= 1) return err;
+  hipLaunchKernelGGL((merge_kernel<D, G>), dim3(a.num_kv_heads, a.batch), dim3(kThreads), 0,
+                     stream, a, SPARSE);
   return (int)hipGetLastError();
 }
 
@@ -394,7 +518,8 @@ template <int D, int G>
 int launch_dg(const AttnLaunch& a, hipStream_t s) {
   const bool paged = a.page_table != nullptr;
   const bool sparse = a.page_idx != nullptr;
-  if (paged) return sparse ? launch_one<D, G, true, true>(a, s) : launch_one<D, G, true, false>(a, s);
+  if (paged)
+    return sparse ? launch_one<D, G, true, true>(a, s) : launch_one<D, G, true, false>(a, s);
   return sparse ? launch_one<D, G, false, true>(a, s) : launch_one<D, G, false, false>(a, s);
 }
 
@@ -411,9 +536,7 @@ int launch_d(const AttnLaunch& a, hipStream_t s) {
 
 }  // namespace
 
-int keys_per_tile(int head_dim, int group) {
-  return (head_dim == 128 && group == 8) ? kWave / 8 : kWave / 4;
-}
+int keys_per_tile(int, int) { return kTileKeys; }
 
 int max_tiles_per_split() { return kMaxTilesPerSplit; }
 
@@ -423,7 +546,5 @@ int launch_decode(const AttnLaunch& a, void* stream) {
   if (a.head_dim == 128) return launch_d<128>(a, s);
   return (int)hipErrorInvalidValue;
 }
-
-static_assert(kMinKeysPerTile == 8, "tile sizes are 8 or 16 keys");
 
 }  // namespace da

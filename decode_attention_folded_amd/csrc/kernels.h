@@ -20,7 +20,6 @@ struct AttnLaunch {
   const void* k_new;         // fp16 [B, Hkv, D] or nullptr
   const void* v_new;
   void* out;                 // fp16 [B, Hq, D]
-  uint32_t* counters;        // [B * Hkv], zero between calls
   float* part_ml;            // [B * Hkv, max_splits, G, 2]
   float* part_o;             // [B * Hkv, max_splits, G, D]
   int32_t batch;
@@ -36,6 +35,7 @@ struct AttnLaunch {
   int32_t tiles_per_split;   // key tiles per workgroup chunk
   int32_t max_splits;        // grid.x
   float scale_log2;          // scale * log2(e)
+  int32_t qk_mfma;           // 1: q.k on the matrix cores, 0: v_dot2 on the VALU
 };
 
 // Split plan shared by the workspace-size query and the launch.

@@ -24,10 +24,10 @@
  *     allocates, frees or synchronises, and keeps no pointer after returning.
  *     All work is enqueued on `stream` (a hipStream_t; NULL = null stream) and
  *     is complete after the caller synchronises that stream.
- *   - Workspace: size it with da_workspace_size / da_quest_workspace_size,
- *     zero-fill it once before its first use (it holds split counters that
- *     every completed call leaves at zero again), and do not share one
- *     workspace between calls that may run concurrently.
+ *   - Workspace: size it with da_workspace_size / da_quest_workspace_size.
+ *     It holds per-split partial results (no state survives a call), needs
+ *     no initialisation, and must not be shared between calls that may run
+ *     concurrently.
  *   - Return value: DA_OK or a negative DA_ERR_* code.  All argument checks run
  *     before anything is enqueued; only DA_ERR_HIP can follow a partial enqueue.
  *     The library never prints and never aborts.
