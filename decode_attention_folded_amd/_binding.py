@@ -170,7 +170,7 @@ def _out_like(q, out):
 
 
 class Workspace:
-    """A device scratch buffer that grows on demand; it holds only per-call
+    """A device scratch buffer that grows on demand.  It holds only per-call
     partial results, so one workspace serves any number of calls issued in
     order on one stream."""
 

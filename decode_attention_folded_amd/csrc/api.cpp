@@ -17,7 +17,7 @@
 namespace {
 
 constexpr int kMaxGridDim = 65535;
-constexpr int kTargetWorkgroups = 2048;  // about 8 per CU on a 256-CU part
+constexpr int kTargetWorkgroups = 512;   // one resident wave of workgroups (2 per CU)
 constexpr int kMinTilesPerSplit = 8;     // at least 2 tiles per wave
 
 bool is_pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }

@@ -70,6 +70,11 @@ __device__ __forceinline__ float lane_xor(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load with the non-temporal hint, for data read exactly once.
+__device__ __forceinline__ f16x8 stream_load(const f16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(p));
+}
+
 // fp32 accumulate of an 8-element fp16 dot product (v_dot2_f32_f16: exact
 // fp16 products, fp32 sums).
 __device__ __forceinline__ float dot8(f16x8 a, f16x8 b, float acc) {

@@ -75,6 +75,7 @@ struct ScoreLaunch {
   int32_t* page_idx;         // [B, Hkv, K]
   int32_t batch, num_kv_heads, group, head_dim;
   int32_t page_shift, meta_max_pages, num_sel;
+  int32_t score_passes;      // set by the launcher
 };
 int launch_score_topk(const ScoreLaunch& p, void* stream);
 int topk_max_pages();

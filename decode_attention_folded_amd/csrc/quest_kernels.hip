@@ -99,15 +99,20 @@ __global__ void __launch_bounds__(kWave) meta_append_kernel(MetaLaunch a) {
 // ------------------------------------------------------------ page score
 
 constexpr int kScoreWaves = 4;
-constexpr int kScoreUnroll = 4;
+constexpr int kScoreDepth = 8;  // page slots per lane per pass (loads in flight)
 
 template <int D>
 struct ScoreShape {
-  static constexpr int LPP = D / 8;                                  // lanes per page
-  static constexpr int PPI = kWave / LPP;                            // pages per wave step
-  static constexpr int PAGES_PER_WG = kScoreWaves * PPI * kScoreUnroll;
+  static constexpr int LPP = D / 8;                 // lanes per page (16-byte chunks)
+  static constexpr int PPI = kWave / LPP;           // pages per wave per slot
+  static constexpr int PAGES_PER_PASS = kScoreWaves * PPI * kScoreDepth;
 };
 
+// One workgroup scores `score_passes` passes of PAGES_PER_PASS consecutive
+// pages of one (b, kv) unit.  Lane (page slot, chunk) loads 16 bytes of the
+// page's min row and 16 of its max row (non-temporal: read once), weighs
+// them with the group's per-channel sums of non-negative / negative queries,
+// and the D/8 lanes of a page add up their partial sums (DPP).
 template <int D, int G>
 __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLaunch a) {
   using SS = ScoreShape<D>;
@@ -126,8 +131,8 @@ __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLa
   L = L < 0 ? 0 : L;
   int n_pages = (L + (1 << shift) - 1) >> shift;
   if (n_pages > a.meta_max_pages) n_pages = a.meta_max_pages;
-  const int p_begin = blockIdx.x * SS::PAGES_PER_WG;
-  if (p_begin >= n_pages) return;
+  const int wg_begin = blockIdx.x * SS::PAGES_PER_PASS * a.score_passes;
+  if (wg_begin >= n_pages) return;
 
   // Per-channel weights: sum of the group's non-negative q_gi (pairs with the
   // max) and of its negative q_gi (pairs with the min).
@@ -149,27 +154,31 @@ __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLa
   }
 
   const f16* mbase = reinterpret_cast<const f16*>(a.meta) + unit * a.meta_max_pages * 2 * D;
-  f16x8 mins[kScoreUnroll], maxs[kScoreUnroll];
-  int pg[kScoreUnroll];
-#pragma unroll
-  for (int u = 0; u < kScoreUnroll; ++u) {
-    const int p = p_begin + (u * kScoreWaves + wave) * PPI + slot;
-    pg[u] = p;
-    const int pp = p < n_pages ? p : p_begin;
-    mins[u] = *reinterpret_cast<const f16x8*>(mbase + (int64_t)pp * 2 * D + 8 * ch);
-    maxs[u] = *reinterpret_cast<const f16x8*>(mbase + (int64_t)pp * 2 * D + D + 8 * ch);
-  }
   float* scores = a.scores + unit * a.meta_max_pages;
+  for (int pass = 0; pass < a.score_passes; ++pass) {
+    const int p0 = wg_begin + pass * SS::PAGES_PER_PASS;
+    if (p0 >= n_pages) break;
+    f16x8 mins[kScoreDepth], maxs[kScoreDepth];
+    int pg[kScoreDepth];
 #pragma unroll
-  for (int u = 0; u < kScoreUnroll; ++u) {
-    float s = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      s = fmaf(wpos[e], (float)maxs[u][e], s);
-      s = fmaf(wneg[e], (float)mins[u][e], s);
+    for (int u = 0; u < kScoreDepth; ++u) {
+      const int p = p0 + (u * kScoreWaves + wave) * PPI + slot;
+      pg[u] = p;
+      const int64_t pp = p < n_pages ? p : p0;  // p0 exists; its score is not stored twice
+      mins[u] = stream_load(mbase + pp * 2 * D + 8 * ch);
+      maxs[u] = stream_load(mbase + pp * 2 * D + D + 8 * ch);
     }
-    s = group_sum<LPP>(s);
-    if (ch == 0 && pg[u] < n_pages) scores[pg[u]] = s;
+#pragma unroll
+    for (int u = 0; u < kScoreDepth; ++u) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s = fmaf(wpos[e], (float)maxs[u][e], s);
+        s = fmaf(wneg[e], (float)mins[u][e], s);
+      }
+      s = group_sum<LPP>(s);
+      if (ch == 0 && pg[u] < n_pages) scores[pg[u]] = s;
+    }
   }
 }
 
@@ -338,7 +347,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
 
 template <int D, int G>
 int launch_score(const ScoreLaunch& a, hipStream_t s) {
-  const int per_wg = ScoreShape<D>::PAGES_PER_WG;
+  const int per_wg = ScoreShape<D>::PAGES_PER_PASS * a.score_passes;
   dim3 grid((a.meta_max_pages + per_wg - 1) / per_wg, a.num_kv_heads, a.batch);
   hipLaunchKernelGGL((page_score_kernel<D, G>), grid, dim3(kWave * kScoreWaves), 0, s, a);
   return (int)hipGetLastError();
@@ -377,8 +386,16 @@ int launch_meta_append(const MetaLaunch& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_score_topk(const ScoreLaunch& a, void* stream) {
+int launch_score_topk(const ScoreLaunch& in, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // passes per workgroup: enough workgroups to fill the chip (~1024), each
+  // streaming as many pages as that allows (at most 8 passes)
+  ScoreLaunch a = in;
+  const int per_pass = a.head_dim == 64 ? ScoreShape<64>::PAGES_PER_PASS
+                                        : ScoreShape<128>::PAGES_PER_PASS;
+  const int64_t total = (int64_t)a.batch * a.num_kv_heads * a.meta_max_pages;
+  int64_t passes = total / (1024 * (int64_t)per_pass);
+  a.score_passes = (int)(passes < 1 ? 1 : (passes > 8 ? 8 : passes));
   int err = a.head_dim == 64 ? launch_score_d<64>(a, s)
           : a.head_dim == 128 ? launch_score_d<128>(a, s)
                               : (int)hipErrorInvalidValue;

@@ -417,3 +417,19 @@ def test_quest_pipeline_end_to_end(da):
         want = oquest.sparse_decode_attention(case.q, case.k, case.v, case.seqlens, want_idx,
                                               page_size, case.scale)
         assert max_err(host(out), want) <= ATOL
+
+
+def test_split_merge_reads_fresh_partials(da):
+    """Calls alternate between different inputs and split counts on one
+    workspace: every merge must see this call's partials, never the previous
+    call's."""
+    cases = [workloads.dense_case(600 + i, 2, 32, 8, 128, 4096, [4096, 3001 - 500 * i])
+             for i in range(3)]
+    wants = [oracle.decode_attention(c.q, c.k, c.v, c.seqlens, c.scale) for c in cases]
+    devs = [(dev(c.q), dev(c.k), dev(c.v), dev(c.seqlens)) for c in cases]
+    ws = da.Workspace()
+    for rep in range(4):
+        for i, (q, k, v, sl) in enumerate(devs):
+            out = da.gqa_decode_attn(q, k, v, sl, workspace=ws, num_splits=[64, 7, 32][i])
+            torch.cuda.synchronize()
+            assert max_err(host(out), wants[i]) <= ATOL, (rep, i)
