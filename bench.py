@@ -54,6 +54,8 @@ def parse_args():
                     choices=["exaone30", "gqa1", "paged", "quest32k", "quest128k"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the 128K Quest/dense leg of the default workload")
     ap.add_argument("--seed", type=int, default=2)
     return ap.parse_args()
 
@@ -270,13 +272,13 @@ def _cpu_baseline(step, data):
     if step.name == "exaone30":
         host = [{k: v.cpu().numpy() for k, v in c.items() if k in TENSORS} for c in data]
         t0 = time.perf_counter()
-        while True:
+        while True:   # whole steps until about 10 s of CPU work
             for c in host:
                 k2, v2 = oracle.append_kv(c["k"], c["v"], c["seqlens"], c["k_new"], c["v_new"])
                 oracle.decode_attention(c["q"], k2, v2, c["seqlens"], 1 / 8.0)
             reps += 1
             bytes_done += step.kv_bytes
-            if time.perf_counter() - t0 > 10.0 or reps >= 3:
+            if time.perf_counter() - t0 > 10.0 or reps >= 30:
                 break
         sample = f"{reps} full 30-layer step(s) (append + repeat_kv attention, fp64)"
     elif step.name in ("gqa1",):
@@ -343,6 +345,93 @@ def _baseline(bytes_done, elapsed, sample):
             "kind": "oracle", "sample": sample, "seconds": round(elapsed, 3)}
 
 
+def kernel_source_digest():
+    """Hash of the attention kernel's sources: the committed counter summary
+    is used only while it was taken on this exact kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_folded_amd", "csrc")
+    for name in ("decode_kernel.hip", "device_common.h", "kernels.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload):
+    """HBM bytes per dominant-kernel launch from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a reference
+    copy), or None if missing or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_kernel_hbm_counters.md")
+    try:
+        text = open(path).read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None
+    entry = data.get("workloads", {}).get(workload)
+    if not entry or data.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def measure(torch, da, dev, step, steps, warmup, flush):
+    """Capture the step, time it (graph replays after a cache flush), then
+    time its launches one by one under HIP events."""
+    for f in step.build_fn:      # eager warm-up allocates every workspace first
+        f()
+    if hasattr(step, "dense_fn"):
+        step.dense_fn()
+    torch.cuda.synchronize()
+    g = capture(torch, step.build_fn)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    step_ms = time_graph(torch, g, steps, warmup, flush)
+    reps = max(1, steps // len(step.build_fn)) if len(step.build_fn) > 1 else steps
+    launch_ms = time_launches(torch, step.build_fn, reps, flush)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms = statistics.median(step_ms)
+    # dominant kernel: the attention launches (every launch of the dense
+    # workloads; the sparse-attention launch of a Quest step)
+    if step.name.startswith("quest"):
+        per = launch_ms[-1]
+    else:
+        per = [x for col in launch_ms for x in col]
+    kern_ms = statistics.median(per)
+    res = {
+        "ms": ms,
+        "gbs": step.kv_bytes / (ms * 1e-3) / 1e9,
+        "kern_ms": kern_ms,
+        "achieved": step.kernel_bytes / (kern_ms * 1e-3) / 1e9,
+        "us_per_step": round(ms * 1e3, 3),
+        "us_p10": round(sorted(step_ms)[len(step_ms) // 10] * 1e3, 3),
+        "us_p90": round(sorted(step_ms)[(len(step_ms) * 9) // 10] * 1e3, 3),
+        "timed_wall_s": round(t_wall, 3),
+        "sum_of_launches_us": round(sum(statistics.median(c) for c in launch_ms) * 1e3, 3),
+    }
+    if hasattr(step, "dense_fn"):
+        dense_ms = statistics.median(time_launches(torch, [step.dense_fn],
+                                                   max(10, steps // 2), flush)[0])
+        res["dense_same_shape_us"] = round(dense_ms * 1e3, 3)
+        res["dense_same_shape_gbs"] = round(step.dense_bytes / (dense_ms * 1e-3) / 1e9, 1)
+        res["dense_same_shape_pct_peak"] = round(
+            100 * step.dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+        res["quest_over_dense_time"] = round(ms / dense_ms, 4)
+        res["byte_model"] = step.byte_model
+        names = (["meta_append"] if step.name == "quest128k" else []) + \
+            ["score_topk", "sparse_attention"]
+        res["stage_us"] = {n: round(statistics.median(col) * 1e3, 3)
+                           for n, col in zip(names, launch_ms)}
+    return res
+
+
+MAKERS = {
+    "exaone30": exaone30, "gqa1": gqa1, "paged": paged,
+    "quest32k": lambda *a: quest(*a, long_ctx=False),
+    "quest128k": lambda *a: quest(*a, long_ctx=True),
+}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -354,70 +443,10 @@ def main():
     da.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    maker = {"exaone30": exaone30, "gqa1": gqa1, "paged": paged,
-             "quest32k": lambda *a: quest(*a, long_ctx=False),
-             "quest128k": lambda *a: quest(*a, long_ctx=True)}[args.workload]
-    step, data = maker(da, torch, args.seed, dev)
     flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
-    # eager warm-up allocates every workspace before capture
-    for f in step.build_fn:
-        f()
-    if hasattr(step, "dense_fn"):
-        step.dense_fn()
-    torch.cuda.synchronize()
-
-    g = capture(torch, step.build_fn)
-
-    # timed region: K graph-replayed steps, then the step's launches one at a
-    # time under HIP events (the dominant kernel's duration)
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    step_ms = time_graph(torch, g, args.steps, args.warmup, flush)
-    reps = max(1, args.steps // len(step.build_fn)) if len(step.build_fn) > 1 else args.steps
-    launch_ms = time_launches(torch, step.build_fn, reps, flush)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-
-    ms = statistics.median(step_ms)
-    gbs = step.kv_bytes / (ms * 1e-3) / 1e9
-    # dominant kernel: the attention launches (every launch of the dense
-    # workloads; the sparse-attention launch of a Quest step)
-    if step.name.startswith("quest"):
-        per = launch_ms[-1]
-    else:
-        per = [x for col in launch_ms for x in col]
-    kern_ms = statistics.median(per)
-    kern_src = "hip events around single launches after a cache flush (median)"
-    achieved = step.kernel_bytes / (kern_ms * 1e-3) / 1e9
-
-    extra = {
-        "us_per_step": round(ms * 1e3, 3),
-        "us_p10": round(sorted(step_ms)[len(step_ms) // 10] * 1e3, 3),
-        "us_p90": round(sorted(step_ms)[(len(step_ms) * 9) // 10] * 1e3, 3),
-        "kv_bytes_per_step": step.kv_bytes,
-        "algorithmic_bytes_per_step": step.algo_bytes,
-        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "cache_flush_between_steps": flush is not None,
-        "graph": "step replayed from one captured HIP graph",
-        "kernel_time_source": kern_src,
-        "timed_wall_s": round(t_wall, 3),
-    }
-    extra["sum_of_launches_us"] = round(sum(statistics.median(c) for c in launch_ms) * 1e3, 3)
-    if hasattr(step, "dense_fn"):
-        dense_ms = statistics.median(time_launches(torch, [step.dense_fn],
-                                                   max(10, args.steps // 2), flush)[0])
-        extra["dense_same_shape_us"] = round(dense_ms * 1e3, 3)
-        extra["dense_same_shape_gbs"] = round(step.dense_bytes / (dense_ms * 1e-3) / 1e9, 1)
-        extra["dense_same_shape_pct_peak"] = round(
-            100 * step.dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
-        extra["quest_over_dense_time"] = round(ms / dense_ms, 4)
-        extra["byte_model"] = step.byte_model
-        names = (["meta_append"] if step.name == "quest128k" else []) + \
-            ["score_topk", "sparse_attention"]
-        extra["stage_us"] = {n: round(statistics.median(col) * 1e3, 3)
-                             for n, col in zip(names, launch_ms)}
+    step, data = MAKERS[args.workload](da, torch, args.seed, dev)
+    r = measure(torch, da, dev, step, args.steps, args.warmup, flush)
 
     # reference copy of known size (scales the FETCH/WRITE counters in the
     # counter runs); not part of the timed region
@@ -425,15 +454,17 @@ def main():
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
+    del src, dst
 
+    traffic = counter_traffic(args.workload)
     line = {
         "metric": "decode-attn KV GB/s (% HBM peak) + us/step",
-        "value": round(gbs, 3),
+        "value": round(r["gbs"], 3),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
+        "ms_per_step": round(r["ms"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -442,19 +473,60 @@ def main():
         "config": step.config,
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved, 3),
+            "achieved": round(r["achieved"], 3),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
             "kernel": step.kernel,
-            "kernel_us": round(kern_ms * 1e3, 3),
+            "kernel_us": round(r["kern_ms"] * 1e3, 3),
             "bytes_per_launch": step.kernel_bytes,
+            "launches_per_step": step.launches,
+            "kernel_time_source": "hip events around single launches after a cache flush "
+                                  "(median)",
         },
+        "us_per_step": r["us_per_step"],
+        "us_p10": r["us_p10"],
+        "us_p90": r["us_p90"],
+        "kv_bytes_per_step": step.kv_bytes,
+        "algorithmic_bytes_per_step": step.algo_bytes,
+        "pct_hbm_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
+        "cache_flush_between_steps": flush is not None,
+        "graph": "step replayed from one captured HIP graph",
+        "timed_wall_s": r["timed_wall_s"],
+        "sum_of_launches_us": r["sum_of_launches_us"],
     }
-    line.update(extra)
+    for key in ("dense_same_shape_us", "dense_same_shape_gbs", "dense_same_shape_pct_peak",
+                "quest_over_dense_time", "byte_model", "stage_us"):
+        if key in r:
+            line[key] = r[key]
+
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step, data, args.seed)
+
+    if args.workload == "exaone30" and not args.no_long_context:
+        # The long-context Quest step (KV + metadata append, page score + top-K,
+        # sparse attention) and dense attention at the same shape, in the same
+        # run: the 32K+ side of the metric.
+        del data
+        torch.cuda.empty_cache()
+        qstep, qdata = MAKERS["quest128k"](da, torch, args.seed, dev)
+        q = measure(torch, da, dev, qstep, max(10, args.steps // 2), 3, flush)
+        line["long_context"] = {
+            "workload": qstep.config["workload"],
+            "quest_us_per_step": q["us_per_step"],
+            "quest_kv_gbs": round(q["gbs"], 1),
+            "stage_us": q["stage_us"],
+            "sparse_attention_gbs": round(q["achieved"], 1),
+            "dense_same_shape_us": q["dense_same_shape_us"],
+            "dense_same_shape_gbs": q["dense_same_shape_gbs"],
+            "dense_same_shape_pct_peak": q["dense_same_shape_pct_peak"],
+            "quest_over_dense_time": q["quest_over_dense_time"],
+            "byte_model_ratio": q["byte_model"]["ratio_model"],
+        }
+        del qdata
+        torch.cuda.empty_cache()
+
     print(json.dumps(line), flush=True)
     return 0
 
