@@ -187,6 +187,7 @@ __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLa
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kRadixBits = 11;
+constexpr int kMaxRankCand = 64;  // boundary candidates resolved by exact ranking
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   // Larger float -> larger key; -0 is folded into +0 first.
@@ -194,28 +195,45 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-enum : uint8_t { kCand = 0, kTake = 1, kDrop = 2 };
-
+// One workgroup per (b, kv).  Thread t holds items i = k * 256 + t (k < R):
+// coalesced loads, and the selected set is kept as an LDS bitmap whose words
+// are written with wave ballots (word of item i = i / 32).
+//   1. keys = order-preserving u32 of the scores; skip the bits shared by the
+//      smallest and largest key;
+//   2. radix passes on 11-bit digits: LDS histogram of the remaining
+//      candidates, boundary digit by a digit-descending block scan; items
+//      above it are taken, below it dropped;
+//   3. once at most 64 candidates tie on the boundary, each is ranked exactly
+//      by (key descending, index ascending); if all 32 key bits are used up
+//      with more candidates, the lowest indices win;
+//   4. the bitmap is compacted in index order (ascending output, -1 pad).
 template <int R>
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
+  static_assert(R >= 8 && R <= 64 && R % 8 == 0, "items per thread");
+  constexpr int NW = R * kTopkThreads / 32;                      // bitmap words
+  constexpr int WPT = (NW + kTopkThreads - 1) / kTopkThreads;    // words per thread
   __shared__ uint32_t hist[1 << kRadixBits];
   __shared__ uint32_t scratch[kTopkWaves];
   __shared__ uint32_t red_min[kTopkWaves], red_max[kTopkWaves];
   __shared__ uint32_t info[3];
+  __shared__ uint32_t selbits[NW];
+  __shared__ uint32_t candbits[NW];
+  __shared__ uint32_t ckey[kMaxRankCand];
+  __shared__ int32_t cidx[kMaxRankCand];
 
   const int tid = threadIdx.x;
+  const int lane = lane_in_wave();
+  const int wave = tid / kWave;
   const int kv = blockIdx.x;
   const int b = blockIdx.y;
   const int64_t unit = (int64_t)b * a.num_kv_heads + kv;
-  const int shift_page = a.page_shift;
   const int K = a.num_sel;
   int32_t* dst = a.page_idx + unit * K;
 
   int L = a.seqlens[b];
   L = L < 0 ? 0 : L;
-  int n_pages = (L + (1 << shift_page) - 1) >> shift_page;
+  int n_pages = (L + (1 << a.page_shift) - 1) >> a.page_shift;
   if (n_pages > a.meta_max_pages) n_pages = a.meta_max_pages;
-
   if (n_pages <= K) {  // every existing page is chosen
     for (int i = tid; i < K; i += kTopkThreads) dst[i] = i < n_pages ? i : -1;
     return;
@@ -223,30 +241,31 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
 
   const float* sc = a.scores + unit * a.meta_max_pages;
   uint32_t key[R];
-  uint8_t st[R];
+  uint64_t cand = 0;   // bit k: item k is still a candidate
+  uint64_t take = 0;   // bit k: item k is chosen
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  // All loads first, unconditionally (clamped index), so they are in flight
+  // together; a load under the validity test would wait for each in turn.
+  float raw[R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const int i = tid * R + j;
-    if (i < n_pages) {
-      key[j] = order_key(sc[i]);
-      st[j] = kCand;
-      kmin = min(kmin, key[j]);
-      kmax = max(kmax, key[j]);
-    } else {
-      key[j] = 0u;
-      st[j] = kDrop;
-    }
+  for (int k = 0; k < R; ++k) raw[k] = sc[min(k * kTopkThreads + tid, n_pages - 1)];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const bool valid = k * kTopkThreads + tid < n_pages;
+    const uint32_t kk = order_key(raw[k]);
+    key[k] = valid ? kk : 0u;
+    cand |= (uint64_t)valid << k;
+    kmin = min(kmin, valid ? kk : 0xFFFFFFFFu);
+    kmax = max(kmax, valid ? kk : 0u);
   }
-  // block min / max of the keys
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, kWave));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, kWave));
   }
-  if (lane_in_wave() == 0) {
-    red_min[tid / kWave] = kmin;
-    red_max[tid / kWave] = kmax;
+  if (lane == 0) {
+    red_min[wave] = kmin;
+    red_max[wave] = kmax;
   }
   __syncthreads();
   kmin = red_min[0];
@@ -258,20 +277,23 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
   }
   const uint32_t diff = kmin ^ kmax;
   int shift = diff ? 32 - __builtin_clz(diff) : 0;  // bits below the common prefix
+  uint32_t need = (uint32_t)K;
+  uint32_t ncand = (uint32_t)n_pages;
 
-  uint32_t need = (uint32_t)K;          // pages still to choose
-  uint32_t ncand = (uint32_t)n_pages;   // candidates: same key prefix above `shift`
-  while (need > 0 && need < ncand && shift > 0) {
+  while (need > 0 && need < ncand && shift > 0 && ncand > (uint32_t)kMaxRankCand) {
     const int nb = shift < kRadixBits ? shift : kRadixBits;
     shift -= nb;
     const uint32_t nbins = 1u << nb;
     for (uint32_t i = tid; i < nbins; i += kTopkThreads) hist[i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-      if (st[j] == kCand) atomicAdd(&hist[(key[j] >> shift) & (nbins - 1)], 1u);
+    for (int k = 0; k < R; ++k) {
+      const bool c = (cand >> k) & 1;
+      if (__ballot(c) != 0)  // wave-uniform: skip slots with no candidate
+        atomicAdd(&hist[(key[k] >> shift) & (nbins - 1)], c ? 1u : 0u);
+    }
     __syncthreads();
-    // Thread t sums a run of `per` digits, taken from the top digit down.
+    // thread t sums a run of `per` digits taken from the top digit down
     const int per = (int)((nbins + kTopkThreads - 1) / kTopkThreads);
     uint32_t run = 0;
     for (int q = 0; q < per; ++q) {
@@ -300,45 +322,106 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
     const uint32_t above = info[1];
     const uint32_t on = info[2];
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      if (st[j] == kCand) {
-        const uint32_t dg = (key[j] >> shift) & (nbins - 1);
-        if (dg > dstar) st[j] = kTake;
-        else if (dg < dstar) st[j] = kDrop;
-      }
+    for (int k = 0; k < R; ++k) {
+      const uint32_t dg = (key[k] >> shift) & (nbins - 1);
+      const uint64_t bit = (uint64_t)1 << k;
+      if (dg > dstar) take |= cand & bit;
+      if (dg != dstar) cand &= ~bit;
     }
     need -= above;
     ncand = on;
+    __syncthreads();  // hist and info are reused by the next pass
+  }
+  if (need >= ncand) {  // the remaining candidates all fit
+    take |= cand;
+    cand = 0;
+  }
+
+  // chosen items -> bitmap (each (slot, wave) owns two words)
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const uint64_t m = __ballot((take >> k) & 1);
+    const uint64_t c = __ballot((cand >> k) & 1);
+    if (lane == 0) {
+      selbits[k * 8 + 2 * wave] = (uint32_t)m;
+      selbits[k * 8 + 2 * wave + 1] = (uint32_t)(m >> 32);
+      candbits[k * 8 + 2 * wave] = (uint32_t)c;
+      candbits[k * 8 + 2 * wave + 1] = (uint32_t)(c >> 32);
+    }
+  }
+  __syncthreads();
+
+  if (need > 0 && need < ncand) {
+    if (ncand <= (uint32_t)kMaxRankCand) {
+      // exact ranking of the boundary candidates: (key desc, index asc)
+      const uint32_t mine = (uint32_t)__builtin_popcountll(cand);
+      uint32_t total;
+      uint32_t pos = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        if ((cand >> k) & 1) {
+          ckey[pos] = key[k];
+          cidx[pos] = k * kTopkThreads + tid;
+          ++pos;
+        }
+      }
+      __syncthreads();
+      if (tid < (int)ncand) {
+        const uint32_t kc = ckey[tid];
+        const int ic = cidx[tid];
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < ncand; ++j) {
+          const uint32_t kj = ckey[j];
+          rank += (kj > kc) || (kj == kc && cidx[j] < ic);
+        }
+        if (rank < need) atomicOr(&selbits[ic >> 5], 1u << (ic & 31));
+      }
+    } else {
+      // all key bits used and more equal keys than places: lowest indices win
+      uint32_t mine = 0;
+#pragma unroll
+      for (int q = 0; q < WPT; ++q) {
+        const int w = tid * WPT + q;
+        if (w < NW) mine += __builtin_popcount(candbits[w]);
+      }
+      uint32_t total;
+      uint32_t rank = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
+#pragma unroll
+      for (int q = 0; q < WPT; ++q) {
+        const int w = tid * WPT + q;
+        if (w >= NW) break;
+        uint32_t bits = candbits[w];
+        uint32_t keep = 0;
+        while (bits != 0 && rank < need) {
+          const uint32_t low = bits & (~bits + 1u);
+          keep |= low;
+          bits ^= low;
+          ++rank;
+        }
+        if (keep) atomicOr(&selbits[w], keep);
+      }
+    }
     __syncthreads();
   }
 
-  // Remaining candidates: all taken if they fit; otherwise their keys are
-  // equal and the lowest page indices win.
-  {
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < R; ++j) mine += st[j] == kCand;
-    uint32_t total;
-    uint32_t rank = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      if (st[j] == kCand) {
-        st[j] = rank < need ? kTake : kDrop;
-        ++rank;
-      }
-    }
-  }
-
-  // Ascending compaction of the chosen pages.
+  // ascending compaction of the bitmap
   uint32_t mine = 0;
 #pragma unroll
-  for (int j = 0; j < R; ++j) mine += st[j] == kTake;
+  for (int q = 0; q < WPT; ++q) {
+    const int w = tid * WPT + q;
+    if (w < NW) mine += __builtin_popcount(selbits[w]);
+  }
   uint32_t total;
   uint32_t pos = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    if (st[j] == kTake) {
-      if (pos < (uint32_t)K) dst[pos] = tid * R + j;
+  for (int q = 0; q < WPT; ++q) {
+    const int w = tid * WPT + q;
+    if (w >= NW) break;
+    uint32_t bits = selbits[w];
+    while (bits != 0) {
+      const int bit = __builtin_ctz(bits);
+      bits &= bits - 1;
+      if (pos < (uint32_t)K) dst[pos] = w * 32 + bit;
       ++pos;
     }
   }
@@ -402,6 +485,7 @@ int launch_score_topk(const ScoreLaunch& in, void* stream) {
   if (err != 0) return err;
   const int P = a.meta_max_pages;
   if (P <= kTopkThreads * 8) return launch_topk<8>(a, s);
+  if (P <= kTopkThreads * 16) return launch_topk<16>(a, s);
   if (P <= kTopkThreads * 32) return launch_topk<32>(a, s);
   if (P <= kTopkThreads * 64) return launch_topk<64>(a, s);
   return (int)hipErrorInvalidValue;

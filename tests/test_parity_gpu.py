@@ -433,3 +433,41 @@ def test_split_merge_reads_fresh_partials(da):
             out = da.gqa_decode_attn(q, k, v, sl, workspace=ws, num_splits=[64, 7, 32][i])
             torch.cuda.synchronize()
             assert max_err(host(out), wants[i]) <= ATOL, (rep, i)
+
+
+def _topk_case(da, scores_kind, n_pages=2048, k_pages=128, seed=700):
+    """Top-K on hand-made metadata: 'equal' makes every page identical (all
+    scores tie), 'many_ties' makes 100 identical pages outscore the rest with
+    K = 50, so more than 64 candidates tie on the boundary."""
+    d, s = 128, 16
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, 4, d), dtype=np.float32).astype(np.float16)
+    meta = np.zeros((1, 1, n_pages, 2, d), np.float16)
+    base = rng.standard_normal((2, d), dtype=np.float32).astype(np.float16)
+    lo, hi = np.minimum(base[0], base[1]), np.maximum(base[0], base[1])
+    if scores_kind == "equal":
+        meta[0, 0, :, 0], meta[0, 0, :, 1] = lo, hi
+    else:
+        noise = rng.standard_normal((n_pages, 2, d), dtype=np.float32).astype(np.float16)
+        meta[0, 0, :, 0] = np.minimum(noise[:, 0], noise[:, 1])
+        meta[0, 0, :, 1] = np.maximum(noise[:, 0], noise[:, 1])
+        hot = rng.choice(n_pages, 100, replace=False)
+        sign = np.sign(q[0].astype(np.float32).sum(0)).astype(np.float16)
+        meta[0, 0, hot, 0] = lo + 3 * sign
+        meta[0, 0, hot, 1] = hi + 3 * sign
+    lens = np.array([n_pages * s], np.int32)
+    idx = host(da.quest_page_score_topk(dev(q), dev(meta), dev(lens), page_size=s,
+                                        budget_tokens=k_pages * s))
+    want = oquest.select_pages(oquest.page_scores(q, meta, lens, s), lens, s, k_pages)
+    return idx, want
+
+
+def test_topk_all_scores_equal(da):
+    idx, want = _topk_case(da, "equal")
+    assert list(want[0, 0]) == list(range(128))
+    assert np.array_equal(idx, want)
+
+
+def test_topk_many_boundary_ties(da):
+    idx, want = _topk_case(da, "many_ties", k_pages=50)
+    assert np.array_equal(idx, want)
