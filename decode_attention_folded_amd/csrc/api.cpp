@@ -157,6 +157,8 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
     return DA_ERR_SHAPE;
   const da::SplitPlan plan = plan_splits(s, max_stream_keys(s, page_idx ? budget_tokens : 0),
                                          num_splits);
+  // one workgroup per (split, b, kv) on a 1-D grid
+  if ((int64_t)plan.max_splits * s.batch * s.hkv > INT32_MAX) return DA_ERR_SHAPE;
   const WsLayout w = ws_layout(s, plan);
   if (workspace == nullptr) return DA_ERR_NULL;
   if (!aligned16(workspace)) return DA_ERR_SHAPE;

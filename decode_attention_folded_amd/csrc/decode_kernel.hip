@@ -8,15 +8,23 @@
 // The Quest variant ([Quest-review], paper sections 3.3-3.5) runs the same
 // loop over the tokens of the chosen pages only.
 //
-// Work decomposition (flash-decode): grid = (splits, Hkv, B).  A workgroup of
-// 4 waves owns a contiguous chunk of `tiles_per_split` 16-key tiles of one
-// (b, kv) unit; its waves take the chunk's tiles round robin.  Each split
-// writes a partial (running max m, sum l, unnormalised o) and a second, small
-// launch merges them (log-sum-exp, in split order).  The kernel boundary is
-// the only synchronisation: merging inside the attention kernel needs either
-// device-scope release/acquire fences (which write back / invalidate the whole
-// L2 of every XCD and cost a third of the runtime) or a device-coherent
-// hand-off, which measured no faster than the extra launch.
+// Work decomposition (flash-decode): a 1-D grid of splits x (B * Hkv) units,
+// unit index fastest.  A workgroup of 4 waves owns a contiguous chunk of
+// `tiles_per_split` 16-key tiles of one (b, kv) unit; its waves take the
+// chunk's tiles round robin.  Workgroups reach the 8 XCDs round robin, so with
+// the unit index fastest every XCD receives the same KV heads of every
+// sequence: sequences of different lengths load the XCDs evenly, which they
+// do not when the split index runs fastest (short sequences would only feed
+// the XCDs of the low split numbers).
+// Each split writes a partial (running max m, sum l, unnormalised o) and a
+// second, small launch merges them (log-sum-exp, in split order).  The kernel
+// boundary is the only synchronisation: merging inside the attention kernel
+// needs either device-scope release/acquire fences (which write back /
+// invalidate the whole L2 of every XCD and cost a third of the runtime) or a
+// hand-off through agent-scope (write-through) stores, an arrival counter and
+// agent-scope loads, which measured no faster than the extra launch on small
+// grids and about 5% slower on large ones (every workgroup must wait for its
+// write-through stores before it retires).
 //
 // Lane layout of one 16-key tile (lane = 0..63):
 //   K: lane holds key (lane % 16), 16-byte channel chunks 4*j + lane/16,
@@ -105,50 +113,71 @@ struct Stage {
   bool kvalid;               // the K key of this lane
 };
 
-// Merge the nsplit partials of one unit (all threads of the workgroup):
-// O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, summed in split order.
-// Loads are issued in batches of 8 so their latencies overlap.
-template <int D, int G>
-__device__ __forceinline__ void merge_splits(const AttnLaunch& a, int64_t unit, int nsplit,
-                                             f16* out, float* s_max, float* s_inv) {
-  constexpr int kBatch = 16;
-  const float* ml = a.part_ml + unit * a.max_splits * G * 2;
+// Merge the split partials of one unit into its G output rows:
+// O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the splits, in split
+// order (log-sum-exp).  Every thread merges whole output elements on its own,
+// reading each split's (m, l) itself, so the loads of a batch issue together;
+// the first batch is read before `get_nsplit` is called (it may wait for the
+// valid length).  Splits past the valid ones are dropped by selects, so stale
+// workspace contents never enter the sums.
+template <int D, int G, typename NSplitFn>
+__device__ __forceinline__ void merge_partials(const AttnLaunch& a, int64_t unit,
+                                               NSplitFn get_nsplit) {
+  constexpr int kIters = (G * D + kThreads - 1) / kThreads;  // 1, 2 or 4
+  constexpr int kBatch = 32 / kIters;                          // splits per load batch
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + unit * a.max_splits * G;
   const float* po = a.part_o + unit * a.max_splits * G * D;
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_in_wave();
-  for (int g = wave; g < G; g += kWaves) {
-    float M = kNegBig;
-    for (int sp = lane; sp < nsplit; sp += kWave) M = fmaxf(M, ml[(sp * G + g) * 2]);
+  f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;
+
+  float M[kIters], O[kIters], S[kIters];
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, kWave));
-    float lsum = 0.0f;
-    for (int sp = lane; sp < nsplit; sp += kWave)
-      lsum += fast_exp2(ml[(sp * G + g) * 2] - M) * ml[(sp * G + g) * 2 + 1];
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) lsum += __shfl_xor(lsum, d, kWave);
-    if (lane == 0) {
-      s_max[g] = M;
-      s_inv[g] = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    }
+  for (int it = 0; it < kIters; ++it) {
+    M[it] = kNegBig;
+    O[it] = 0.0f;
+    S[it] = 0.0f;
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int g = i / D;
-    const float M = s_max[g];
-    float o = 0.0f;
-    for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
-      float mv[kBatch], ov[kBatch];
+  int nsplit = 0;
+  for (int s0 = 0;; s0 += kBatch) {
+    float2 mv[kIters][kBatch];
+    float ov[kIters][kBatch];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int i = min((int)threadIdx.x + it * kThreads, G * D - 1);
+      const int g = i / D;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int sp = min(s0 + u, nsplit - 1);
-        mv[u] = ml[(sp * G + g) * 2];
-        ov[u] = po[(int64_t)sp * G * D + i];
+        const int sp = min(s0 + u, a.max_splits - 1);
+        mv[it][u] = ml[sp * G + g];
+        ov[it][u] = po[(int64_t)sp * G * D + i];
       }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (s0 + u < nsplit) o = fmaf(fast_exp2(mv[u] - M), ov[u], o);
     }
-    out[i] = (f16)(o * s_inv[g]);
+    if (s0 == 0) {
+      nsplit = get_nsplit();
+      if (nsplit <= 1) return;  // the attention kernel wrote the output
+    }
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      float bm = M[it];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) bm = s0 + u < nsplit ? fmaxf(bm, mv[it][u].x) : bm;
+      const float f = fast_exp2(M[it] - bm);
+      float o = O[it] * f, l = S[it] * f;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float w = s0 + u < nsplit ? fast_exp2(mv[it][u].x - bm) : 0.0f;
+        o = fmaf(w, s0 + u < nsplit ? ov[it][u] : 0.0f, o);
+        l = fmaf(w, s0 + u < nsplit ? mv[it][u].y : 0.0f, l);
+      }
+      M[it] = bm;
+      O[it] = o;
+      S[it] = l;
+    }
+    if (s0 + kBatch >= nsplit) break;
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int i = (int)threadIdx.x + it * kThreads;
+    if (i < G * D) out[i] = (f16)(S[it] > 0.0f ? O[it] / S[it] : 0.0f);
   }
 }
 
@@ -173,13 +202,60 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   const int rv = lane & 7;         // V key slots rv, rv + 8
   const int cv = lane >> 3;        // V chunk group (0..7)
   const bool upper = (lane & 8) != 0;
-  const int split = blockIdx.x;
-  const int kv = blockIdx.y;
-  const int b = blockIdx.z;
   const int hkv = a.num_kv_heads;
-  const int64_t unit = (int64_t)b * hkv + kv;
+  // grid < 2^31 workgroups (checked on the host): 32-bit index arithmetic
+  const uint32_t n_units = (uint32_t)a.batch * (uint32_t)hkv;
+  const uint32_t split_u = blockIdx.x / n_units;
+  const uint32_t unit_u = blockIdx.x - split_u * n_units;
+  const uint32_t b_u = unit_u / (uint32_t)hkv;
+  const int split = (int)split_u;
+  const int64_t unit = unit_u;
+  const int b = (int)b_u;
+  const int kv = (int)(unit_u - b_u * (uint32_t)hkv);
   const int shift = a.page_shift;
   const int page_mask = (1 << shift) - 1;
+  const int tile_begin = split * a.tiles_per_split;
+  const int key_begin = tile_begin * kTileKeys;
+  const int page0 = key_begin >> shift;
+
+  // Inputs that do not depend on the valid length: the folded queries and the
+  // raw page-list entries of the whole chunk (clamped indices; checked once
+  // the length is known).
+  const f16* qb = reinterpret_cast<const f16*>(a.q) + unit * G * D;
+  // MFMA A operand: row i of chain c is query g = (4c + i % 4) mod G; the lane
+  // holds row lane % 16 over the k-slots of chunk 4j + ck.
+  f16x8 qa[QK_MFMA ? GC : 1][QK_MFMA ? NCK : 1];
+  // VALU operand: all G rows over the lane's K channels.
+  f16x8 qv[QK_MFMA ? 1 : G][QK_MFMA ? 1 : NCK];
+  if constexpr (QK_MFMA) {
+#pragma unroll
+    for (int cch = 0; cch < GC; ++cch) {
+      const int g = (4 * cch + (rk & 3)) % G;
+#pragma unroll
+      for (int j = 0; j < NCK; ++j)
+        qa[cch][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < NCK; ++j)
+        qv[g][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
+  }
+  // Entry i of the chunk's page list: the chosen logical page (selected-page
+  // stream) and/or the physical page (paged cache), read with clamped indices.
+  constexpr int kListIters = (PAGED || SPARSE) ? (kMaxChunkPages + kThreads - 1) / kThreads : 0;
+  int raw_logical[kListIters > 0 ? kListIters : 1];
+  int raw_phys[kListIters > 0 ? kListIters : 1];
+#pragma unroll
+  for (int r = 0; r < kListIters; ++r) {
+    const int i = (int)threadIdx.x + r * kThreads;
+    int logical = page0 + i;
+    if constexpr (SPARSE) logical = a.page_idx[unit * a.num_sel + min(page0 + i, a.num_sel - 1)];
+    raw_logical[r] = logical;
+    if constexpr (PAGED)
+      raw_phys[r] = a.page_table[(int64_t)b * a.max_pages + min(max(logical, 0), a.max_pages - 1)];
+  }
 
   const StreamInfo si = stream_info(a, b, SPARSE);
   const int L = si.L;
@@ -196,37 +272,34 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   }
 
   const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
-  const int tile_begin = split * a.tiles_per_split;
   const int tile_end = min(tile_begin + a.tiles_per_split, n_tiles);
-  const int key_begin = tile_begin * kTileKeys;
   const int key_last = min(tile_end * kTileKeys, n_keys) - 1;
-  const int page0 = key_begin >> shift;
 
   // Page lists of this chunk into LDS: the physical page of each logical page
   // (paged cache) and/or the chosen logical pages (selected-page stream).
   // Entries that do not name an existing page become -1.
   if constexpr (PAGED || SPARSE) {
     const int npg = (key_last >> shift) - page0 + 1;
-    for (int i = threadIdx.x; i < npg; i += kThreads) {
-      int logical = page0 + i;
-      if constexpr (SPARSE) {
-        logical = a.page_idx[unit * a.num_sel + page0 + i];
-        if (logical < 0 || logical >= n_pages_L) logical = -1;
-      }
-      int entry = logical;
-      if constexpr (PAGED) {
-        int phys = -1;
-        if (logical >= 0 && logical < a.max_pages) {
-          phys = a.page_table[(int64_t)b * a.max_pages + logical];
-          if (phys < 0 || phys >= a.num_pages) phys = -1;
-        }
+#pragma unroll
+    for (int r = 0; r < kListIters; ++r) {
+      const int i = (int)threadIdx.x + r * kThreads;
+      if (i < npg) {
+        int logical = raw_logical[r];
         if constexpr (SPARSE) {
-          s_phys[i] = phys;
-        } else {
-          entry = phys;
+          if (logical < 0 || logical >= n_pages_L) logical = -1;
         }
+        int entry = logical;
+        if constexpr (PAGED) {
+          int phys = raw_phys[r];
+          if (logical < 0 || logical >= a.max_pages || phys < 0 || phys >= a.num_pages) phys = -1;
+          if constexpr (SPARSE) {
+            s_phys[i] = phys;
+          } else {
+            entry = phys;
+          }
+        }
+        s_page[i] = entry;
       }
-      s_page[i] = entry;
     }
     __syncthreads();
   }
@@ -249,29 +322,6 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   const bool has_new = a.k_new != nullptr;
   const f16* knew_row = has_new ? reinterpret_cast<const f16*>(a.k_new) + unit * D : nullptr;
   const f16* vnew_row = has_new ? reinterpret_cast<const f16*>(a.v_new) + unit * D : nullptr;
-
-  // Folded queries of this KV head.
-  const f16* qb = reinterpret_cast<const f16*>(a.q) + unit * G * D;
-  // MFMA A operand: row i of chain c is query g = (4c + i % 4) mod G; the lane
-  // holds row lane % 16 over the k-slots of chunk 4j + ck.
-  f16x8 qa[QK_MFMA ? GC : 1][QK_MFMA ? NCK : 1];
-  // VALU operand: all G rows over the lane's K channels.
-  f16x8 qv[QK_MFMA ? 1 : G][QK_MFMA ? 1 : NCK];
-  if constexpr (QK_MFMA) {
-#pragma unroll
-    for (int cch = 0; cch < GC; ++cch) {
-      const int g = (4 * cch + (rk & 3)) % G;
-#pragma unroll
-      for (int j = 0; j < NCK; ++j)
-        qa[cch][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < NCK; ++j)
-        qv[g][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
-  }
 
   float m[G], l[G], acc[G][NV];
 #pragma unroll
@@ -505,23 +555,18 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   }
 }
 
-// Merge launch: one workgroup per (b, kv) unit.
+// Merge kernel: one workgroup per (b, kv) unit.
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) merge_kernel(AttnLaunch a, bool sparse) {
-  __shared__ float s_max[G];
-  __shared__ float s_inv[G];
   const int kv = blockIdx.x;
   const int b = blockIdx.y;
   const int64_t unit = (int64_t)b * a.num_kv_heads + kv;
-  const StreamInfo si = stream_info(a, b, sparse);
-  if (si.nsplit <= 1) return;  // the attention kernel wrote the output
-  merge_splits<D, G>(a, unit, si.nsplit, reinterpret_cast<f16*>(a.out) + unit * G * D, s_max,
-                     s_inv);
+  merge_partials<D, G>(a, unit, [&] { return stream_info(a, b, sparse).nsplit; });
 }
 
 template <int D, int G, bool PAGED, bool SPARSE>
 int launch_one(const AttnLaunch& a, hipStream_t stream) {
-  dim3 grid(a.max_splits, a.num_kv_heads, a.batch);
+  const dim3 grid((uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads);
   if (a.qk_mfma) {
     hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, true>), grid, dim3(kThreads), 0,
                        stream, a);

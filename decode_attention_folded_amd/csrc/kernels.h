@@ -33,7 +33,7 @@ struct AttnLaunch {
   int64_t num_pages;         // pool size; page-table entries outside [0, num_pages) are skipped
   int32_t num_sel;           // K pages per (b, kv) in the selected-page stream
   int32_t tiles_per_split;   // key tiles per workgroup chunk
-  int32_t max_splits;        // grid.x
+  int32_t max_splits;        // splits per (b, kv) unit; the grid is max_splits * B * Hkv
   float scale_log2;          // scale * log2(e)
   int32_t qk_mfma;           // 1: q.k on the matrix cores, 0: v_dot2 on the VALU
 };

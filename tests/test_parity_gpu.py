@@ -89,6 +89,16 @@ def test_dense_split_counts(da, splits):
     assert max_err(got, want) <= ATOL
 
 
+@pytest.mark.parametrize("d,g,splits", [(64, 1, 100), (64, 8, 40), (128, 8, 50), (128, 2, 33)])
+def test_merge_many_splits(da, d, g, splits):
+    """Split counts above one merge batch (32, 16 or 8 partials per load
+    batch depending on G * D), with one sequence too short to fill them."""
+    case = workloads.dense_case(9 + g, 3, 2 * g, 2, d, 1600, [1600, 1111, 20])
+    got, _, _ = run_dense(da, case, num_splits=splits)
+    want = oracle.decode_attention(case.q, case.k, case.v, case.seqlens, case.scale)
+    assert max_err(got, want) <= ATOL
+
+
 def test_dense_bitwise_deterministic(da):
     case = workloads.dense_case(8, 2, 32, 8, 128, 3000, [3000, 2047])
     a, _, _ = run_dense(da, case)
