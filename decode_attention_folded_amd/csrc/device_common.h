@@ -87,15 +87,52 @@ __device__ __forceinline__ float dot8(f16x8 a, f16x8 b, float acc) {
   return acc;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  // lanes outside the masks, or whose source lane does not exist, read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+constexpr int kDppRowShr1 = 0x111;     // lane i <- lane i-1 within each 16-lane row
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr3 = 0x113;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> every lane of the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> every lane of rows 2 and 3
+
+// Inclusive prefix sum over the 64 lanes of a wave, in DPP steps (no LDS
+// round trips): prefix over 4 lanes from three row shifts of the input, then
+// 8 and 16 lanes with bank-masked row shifts, then the row totals carried by
+// the row broadcasts of lanes 15 and 31.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = lane_in_wave();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
+  uint32_t x = v + dpp_u32<kDppRowShr1, 0xF, 0xF>(v) + dpp_u32<kDppRowShr2, 0xF, 0xF>(v) +
+               dpp_u32<kDppRowShr3, 0xF, 0xF>(v);
+  x += dpp_u32<kDppRowShr4, 0xF, 0xE>(x);     // lanes 4..15 of each row
+  x += dpp_u32<kDppRowShr8, 0xF, 0xC>(x);     // lanes 8..15 of each row
+  x += dpp_u32<kDppRowBcast15, 0xA, 0xF>(x);  // rows 1 and 3
+  x += dpp_u32<kDppRowBcast31, 0xC, 0xF>(x);  // rows 2 and 3
+  return x;
+}
+
+// Reduction over the 64 lanes of a wave with an associative, commutative op;
+// the result is wave-uniform.  DPP within each 16-lane row, then the four row
+// results through readlane.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  uint32_t x = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppXor1, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppXor2, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppHalfMirror, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppMirror, 0xF, 0xF, false));
+  return op(op((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16)),
+            op((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
 // Exclusive prefix sum over a block of NWAVES waves; *total gets the block

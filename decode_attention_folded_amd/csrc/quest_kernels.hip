@@ -22,9 +22,12 @@
 //   topk_kernel         one workgroup per (b, kv): scores held in registers as
 //                       order-preserving u32 keys; radix select on 11-bit
 //                       digits below the common prefix of the min and max key,
-//                       then an index-order scan for exact ties and for the
-//                       ascending compaction.  Integer-only decisions, so the
-//                       chosen set is deterministic.
+//                       exact ranking of the last candidates in registers, an
+//                       index-order scan for exact ties and the ascending
+//                       compaction.  Integer-only decisions, so the chosen set
+//                       is deterministic.  (Bit-serial passes without atomics
+//                       measured slower: 7-8 barrier-bound passes cost more
+//                       than 2-3 histogram passes.)
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -213,13 +216,14 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
   constexpr int NW = R * kTopkThreads / 32;                      // bitmap words
   constexpr int WPT = (NW + kTopkThreads - 1) / kTopkThreads;    // words per thread
   __shared__ uint32_t hist[1 << kRadixBits];
+  __shared__ uint32_t info[3];
   __shared__ uint32_t scratch[kTopkWaves];
   __shared__ uint32_t red_min[kTopkWaves], red_max[kTopkWaves];
-  __shared__ uint32_t info[3];
   __shared__ uint32_t selbits[NW];
   __shared__ uint32_t candbits[NW];
   __shared__ uint32_t ckey[kMaxRankCand];
   __shared__ int32_t cidx[kMaxRankCand];
+  __shared__ uint32_t n_listed;
 
   const int tid = threadIdx.x;
   const int lane = lane_in_wave();
@@ -239,6 +243,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
     return;
   }
 
+  if (tid == 0) n_listed = 0;  // ordered before its use by the barriers below
   const float* sc = a.scores + unit * a.meta_max_pages;
   uint32_t key[R];
   uint64_t cand = 0;   // bit k: item k is still a candidate
@@ -258,11 +263,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
     kmin = min(kmin, valid ? kk : 0xFFFFFFFFu);
     kmax = max(kmax, valid ? kk : 0u);
   }
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, kWave));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, kWave));
-  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
   if (lane == 0) {
     red_min[wave] = kmin;
     red_max[wave] = kmax;
@@ -353,28 +355,31 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
 
   if (need > 0 && need < ncand) {
     if (ncand <= (uint32_t)kMaxRankCand) {
-      // exact ranking of the boundary candidates: (key desc, index asc)
-      const uint32_t mine = (uint32_t)__builtin_popcountll(cand);
-      uint32_t total;
-      uint32_t pos = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
+      // exact ranking of the boundary candidates by (key desc, index asc):
+      // list them (slot order is irrelevant), then wave 0 holds one per lane
+      // and compares against every other through readlane
 #pragma unroll
       for (int k = 0; k < R; ++k) {
         if ((cand >> k) & 1) {
-          ckey[pos] = key[k];
-          cidx[pos] = k * kTopkThreads + tid;
-          ++pos;
+          const uint32_t pos = atomicAdd(&n_listed, 1u);
+          if (pos < (uint32_t)kMaxRankCand) {  // ncand <= 64 candidates exist
+            ckey[pos] = key[k];
+            cidx[pos] = k * kTopkThreads + tid;
+          }
         }
       }
       __syncthreads();
-      if (tid < (int)ncand) {
-        const uint32_t kc = ckey[tid];
-        const int ic = cidx[tid];
+      if (wave == 0) {
+        const bool has = lane < (int)ncand;
+        const uint32_t kc = has ? ckey[lane] : 0u;
+        const int ic = has ? cidx[lane] : 0x7FFFFFFF;
         uint32_t rank = 0;
-        for (uint32_t j = 0; j < ncand; ++j) {
-          const uint32_t kj = ckey[j];
-          rank += (kj > kc) || (kj == kc && cidx[j] < ic);
+        for (int j = 0; j < (int)ncand; ++j) {
+          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kc, j);
+          const int ij = __builtin_amdgcn_readlane(ic, j);
+          rank += (kj > kc) || (kj == kc && ij < ic);
         }
-        if (rank < need) atomicOr(&selbits[ic >> 5], 1u << (ic & 31));
+        if (has && rank < need) atomicOr(&selbits[ic >> 5], 1u << (ic & 31));
       }
     } else {
       // all key bits used and more equal keys than places: lowest indices win
