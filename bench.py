@@ -20,12 +20,18 @@ batch of synthetic inputs already resident in HBM:
                dense at the same shape).
 
 Before every timed step a 1 GiB buffer is written (outside the step's events)
-so that neither L2 nor the 256 MiB Infinity Cache holds the inputs.  Step time
-is the median over the K steps of HIP events around the graph replay; the
-dominant kernel's duration comes from events captured between the kernels
-inside the same graph.  `value` is the KV bytes the step must read divided by
-the step time.  The CPU baseline is the fp64 NumPy oracle (1 BLAS thread) on
-a bounded sample of the same workload, timed on the host.
+so that neither L2 nor the 256 MiB Infinity Cache holds the inputs.  The step
+is captured once in a HIP graph; its time is the median over the K replays of
+HIP events around the replay on the launching stream.  `value` is the KV bytes
+the step must read divided by the step time.  A step is made of stages (the
+dense workloads: one stage of attention calls; Quest: KV + metadata append,
+page score + top-K, sparse attention).  The roofline entry is the dominant
+stage: its algorithmic bytes divided by its time, which for a one-stage step
+is the step time itself and otherwise the median over replays of the stage's
+own graph after a flush.  One attention call runs the attention kernel and
+the small split-merge kernel (or the score and top-K kernels), so both count.
+The CPU baseline is the fp64 NumPy oracle (1 BLAS thread) on a bounded sample
+of the same workload, timed on the host.
 """
 
 import argparse
@@ -63,20 +69,26 @@ def parse_args():
 # ---------------------------------------------------------------- workloads
 
 
-class Step:
-    """A captured step: graph, the events inside it, byte accounting."""
+class Stage:
+    """Calls captured into one graph: `calls` launches of one C-ABI entry
+    point (each running `kernels`), moving `bytes` algorithmic bytes."""
 
-    def __init__(self, name, config, kv_bytes, algo_bytes, launches, kernel, kernel_bytes,
-                 build_fn, marks):
+    def __init__(self, name, fns, nbytes, kernels):
+        self.name = name
+        self.fns = fns
+        self.bytes = nbytes
+        self.kernels = kernels
+
+
+class Step:
+    """One pass of the hot path: its stages and its byte accounting."""
+
+    def __init__(self, name, config, kv_bytes, algo_bytes, stages):
         self.name = name
         self.config = config
-        self.kv_bytes = kv_bytes            # K/V bytes the step must read (the metric)
+        self.kv_bytes = kv_bytes            # K/V (and metadata) bytes the step must read
         self.algo_bytes = algo_bytes        # every byte the method must move
-        self.launches = launches            # dominant-kernel launches per step
-        self.kernel = kernel                # dominant kernel (name stem)
-        self.kernel_bytes = kernel_bytes    # algorithmic bytes per dominant launch
-        self.build_fn = build_fn            # enqueues one step on the current stream
-        self.marks = marks                  # (label, index of launch) for event pairs
+        self.stages = stages
 
 
 def exaone30(da, torch, seed, dev):
@@ -100,9 +112,9 @@ def exaone30(da, torch, seed, dev):
     cfg = {"workload": "exaone1.2b_30layer_decode_hq32_hkv8_d64_cap4096_len3000_append",
            "layers": layers, "batch": 1, "num_q_heads": hq, "num_kv_heads": hkv,
            "head_dim": d, "capacity": cap, "valid_len": L, "dtype_cache": "fp16"}
-    return Step("exaone30", cfg, layers * kv_layer, layers * per_launch, layers,
-                "decode_kernel", per_launch, [lambda l=l: one(l) for l in range(layers)],
-                None), data
+    st = Stage("attention", [lambda l=l: one(l) for l in range(layers)], layers * per_launch,
+               "decode_kernel + merge_kernel (gqa_decode_attn)")
+    return Step("exaone30", cfg, layers * kv_layer, layers * per_launch, [st]), data
 
 
 def gqa1(da, torch, seed, dev):
@@ -118,8 +130,9 @@ def gqa1(da, torch, seed, dev):
     kv = 2 * hkv * L * d * 2
     cfg = {"workload": "gqa_decode_b1_hq32_hkv8_d64_ctx4096", "batch": 1, "num_q_heads": hq,
            "num_kv_heads": hkv, "head_dim": d, "valid_len": L}
-    return Step("gqa1", cfg, kv, kv + 2 * hq * d * 2, 1, "decode_kernel",
-                kv + 2 * hq * d * 2, [one], None), c
+    st = Stage("attention", [one], kv + 2 * hq * d * 2,
+               "decode_kernel + merge_kernel (gqa_decode_attn)")
+    return Step("gqa1", cfg, kv, kv + 2 * hq * d * 2, [st]), c
 
 
 def paged(da, torch, seed, dev):
@@ -140,7 +153,8 @@ def paged(da, torch, seed, dev):
     cfg = {"workload": "paged_gqa_decode_b64_hq32_hkv8_d128_s16_len1k-32k", "batch": b,
            "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "page_size": s,
            "total_tokens": int(np.sum(lens))}
-    return Step("paged", cfg, kv, per, 1, "decode_kernel", per, [one], None), c
+    st = Stage("attention", [one], per, "decode_kernel + merge_kernel (gqa_decode_attn)")
+    return Step("paged", cfg, kv, per, [st]), c
 
 
 def quest(da, torch, seed, dev, long_ctx):
@@ -184,13 +198,22 @@ def quest(da, torch, seed, dev, long_ctx):
     sel_bytes = units * k_sel * s * 2 * d * 2
     dense_bytes = units * L * 2 * d * 2
     kv_bytes = meta_bytes + sel_bytes
-    algo = kv_bytes + 2 * units * P * 4 + units * k_sel * 4 + 2 * b * hq * d * 2
-    fns = ([append] if long_ctx else []) + [select, attend]
+    qo_bytes = 2 * b * hq * d * 2
+    score_bytes = meta_bytes + 2 * units * P * 4 + units * k_sel * 4 + b * hq * d * 2
+    attend_bytes = sel_bytes + qo_bytes + units * k_sel * 4
+    # append: the new K/V row (read + write) and the touched page's min/max
+    append_bytes = units * (2 * 2 * d * 2 + 2 * 2 * d * 2)
+    algo = score_bytes + attend_bytes + (append_bytes if long_ctx else 0)
+    stages = ([Stage("meta_append", [append], append_bytes, "meta_append_kernel")]
+              if long_ctx else [])
+    stages += [Stage("score_topk", [select], score_bytes,
+                     "page_score_kernel + topk_kernel (quest_page_score_topk)"),
+               Stage("sparse_attention", [attend], attend_bytes,
+                     "decode_kernel + merge_kernel (quest_sparse_decode_attn)")]
     cfg = {"workload": name, "batch": b, "num_q_heads": hq, "num_kv_heads": hkv,
            "head_dim": d, "seq_len": L, "page_size": s, "budget_tokens": budget,
            "k_pages": k_sel}
-    st = Step("quest128k" if long_ctx else "quest32k", cfg, kv_bytes, algo, 1,
-              "decode_kernel", sel_bytes + 2 * b * hq * d * 2 + units * k_sel * 4, fns, None)
+    st = Step("quest128k" if long_ctx else "quest32k", cfg, kv_bytes, algo, stages)
     st.dense_fn = dense
     st.dense_bytes = dense_bytes
     st.byte_model = {"meta_bytes": meta_bytes, "selected_bytes": sel_bytes,
@@ -216,42 +239,25 @@ def capture(torch, fns):
     return g
 
 
-def time_graph(torch, g, steps, warmup, flush):
-    """Replay the graph warmup + steps times (cache flush before each, outside
-    the events); returns per-step ms."""
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    step_ms = []
+def time_stages(torch, graphs, steps, warmup, flush):
+    """Replay the stage graphs back to back, warmup + steps times, with a cache
+    flush before each step (outside the events) and HIP events between the
+    stages on the launching stream.  Returns per-step ms and per-stage ms."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
+    step_ms, stage_ms = [], [[] for _ in graphs]
     for i in range(warmup + steps):
         if flush is not None:
             flush.zero_()
-        a.record()
-        g.replay()
-        b.record()
+        ev[0].record()
+        for j, g in enumerate(graphs):
+            g.replay()
+            ev[j + 1].record()
+        torch.cuda.synchronize()
         if i >= warmup:
-            torch.cuda.synchronize()
-            step_ms.append(a.elapsed_time(b))
-    torch.cuda.synchronize()
-    return step_ms
-
-
-def time_launches(torch, fns, reps, flush):
-    """HIP events around single launches on the launching stream.  The 1 GiB
-    flush enqueued just before keeps the GPU busy while the host enqueues the
-    launch, so the event pair brackets the kernel itself."""
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    per = [[] for _ in fns]
-    for r in range(reps):
-        for i, f in enumerate(fns):
-            if flush is not None:
-                flush.zero_()
-            a.record()
-            f()
-            b.record()
-            torch.cuda.synchronize()
-            per[i].append(a.elapsed_time(b))
-    return per
+            step_ms.append(ev[0].elapsed_time(ev[-1]))
+            for j in range(len(graphs)):
+                stage_ms[j].append(ev[j].elapsed_time(ev[j + 1]))
+    return step_ms, stage_ms
 
 
 def cpu_baseline(step, data, seed):
@@ -346,22 +352,23 @@ def _baseline(bytes_done, elapsed, sample):
 
 
 def kernel_source_digest():
-    """Hash of the attention kernel's sources: the committed counter summary
-    is used only while it was taken on this exact kernel."""
+    """Hash of the kernel sources: the committed counter summary is used only
+    while it was taken on these exact kernels."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_folded_amd", "csrc")
-    for name in ("decode_kernel.hip", "device_common.h", "kernels.h"):
+    for name in ("decode_kernel.hip", "quest_kernels.hip", "device_common.h", "kernels.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def counter_traffic(workload):
-    """HBM bytes per dominant-kernel launch from the committed rocprofv3
-    counter summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a reference
-    copy), or None if missing or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", "decode_kernel_hbm_counters.md")
+    """HBM bytes per call of the dominant stage (its kernels summed) from the
+    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE runs,
+    scaled by a reference copy), or None if missing or taken on different
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
     try:
         text = open(path).read()
         blob = text.split("```json", 1)[1].split("```", 1)[0]
@@ -371,57 +378,58 @@ def counter_traffic(workload):
     entry = data.get("workloads", {}).get(workload)
     if not entry or data.get("kernel_source_digest") != kernel_source_digest():
         return None
-    return entry.get("bytes_per_launch")
+    return entry.get("bytes_per_call")
 
 
 def measure(torch, da, dev, step, steps, warmup, flush):
-    """Capture the step, time it (graph replays after a cache flush), then
-    time its launches one by one under HIP events."""
-    for f in step.build_fn:      # eager warm-up allocates every workspace first
-        f()
+    """Time the step as one captured graph (cache flush before every replay,
+    HIP events around it); with several stages, time each stage's own graph
+    the same way to find the dominant one.  A single-stage step is its own
+    dominant stage, timed in the same loop."""
+    for st in step.stages:       # eager warm-up allocates every workspace first
+        for f in st.fns:
+            f()
     if hasattr(step, "dense_fn"):
         step.dense_fn()
     torch.cuda.synchronize()
-    g = capture(torch, step.build_fn)
+    g_step = capture(torch, [f for st in step.stages for f in st.fns])
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    step_ms = time_graph(torch, g, steps, warmup, flush)
-    reps = max(1, steps // len(step.build_fn)) if len(step.build_fn) > 1 else steps
-    launch_ms = time_launches(torch, step.build_fn, reps, flush)
+    step_ms = time_stages(torch, [g_step], steps, warmup, flush)[0]
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     ms = statistics.median(step_ms)
-    # dominant kernel: the attention launches (every launch of the dense
-    # workloads; the sparse-attention launch of a Quest step)
-    if step.name.startswith("quest"):
-        per = launch_ms[-1]
+    if len(step.stages) == 1:
+        med = [ms]
     else:
-        per = [x for col in launch_ms for x in col]
-    kern_ms = statistics.median(per)
+        med = []
+        for st in step.stages:
+            g = capture(torch, st.fns)
+            med.append(statistics.median(time_stages(torch, [g], max(10, steps // 2), 2,
+                                                     flush)[0]))
+    dom = max(range(len(med)), key=lambda j: med[j])
+    dst = step.stages[dom]
     res = {
         "ms": ms,
         "gbs": step.kv_bytes / (ms * 1e-3) / 1e9,
-        "kern_ms": kern_ms,
-        "achieved": step.kernel_bytes / (kern_ms * 1e-3) / 1e9,
+        "dominant": dst,
+        "stage_ms": med[dom],
+        "achieved": dst.bytes / (med[dom] * 1e-3) / 1e9,
         "us_per_step": round(ms * 1e3, 3),
         "us_p10": round(sorted(step_ms)[len(step_ms) // 10] * 1e3, 3),
         "us_p90": round(sorted(step_ms)[(len(step_ms) * 9) // 10] * 1e3, 3),
         "timed_wall_s": round(t_wall, 3),
-        "sum_of_launches_us": round(sum(statistics.median(c) for c in launch_ms) * 1e3, 3),
+        "stage_us": {st.name: round(m * 1e3, 3) for st, m in zip(step.stages, med)},
     }
     if hasattr(step, "dense_fn"):
-        dense_ms = statistics.median(time_launches(torch, [step.dense_fn],
-                                                   max(10, steps // 2), flush)[0])
+        g = capture(torch, [step.dense_fn])
+        dense_ms = statistics.median(time_stages(torch, [g], max(10, steps // 2), 2, flush)[0])
         res["dense_same_shape_us"] = round(dense_ms * 1e3, 3)
         res["dense_same_shape_gbs"] = round(step.dense_bytes / (dense_ms * 1e-3) / 1e9, 1)
         res["dense_same_shape_pct_peak"] = round(
             100 * step.dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
         res["quest_over_dense_time"] = round(ms / dense_ms, 4)
         res["byte_model"] = step.byte_model
-        names = (["meta_append"] if step.name == "quest128k" else []) + \
-            ["score_topk", "sparse_attention"]
-        res["stage_us"] = {n: round(statistics.median(col) * 1e3, 3)
-                           for n, col in zip(names, launch_ms)}
     return res
 
 
@@ -478,12 +486,16 @@ def main():
             "unit": "GB/s",
             "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": step.kernel,
-            "kernel_us": round(r["kern_ms"] * 1e3, 3),
-            "bytes_per_launch": step.kernel_bytes,
-            "launches_per_step": step.launches,
-            "kernel_time_source": "hip events around single launches after a cache flush "
-                                  "(median)",
+            "kernel": r["dominant"].kernels,
+            "stage": r["dominant"].name,
+            "calls_per_step": len(r["dominant"].fns),
+            "us_per_call": round(r["stage_ms"] * 1e3 / len(r["dominant"].fns), 3),
+            "bytes_per_call": r["dominant"].bytes // len(r["dominant"].fns),
+            "time_source": ("HIP events around the step's graph replay in the timed "
+                            "region (median over steps), divided by its calls"
+                            if len(step.stages) == 1 else
+                            "HIP events around replays of the stage's own graph after a "
+                            "cache flush (median), divided by its calls"),
         },
         "us_per_step": r["us_per_step"],
         "us_p10": r["us_p10"],
@@ -492,12 +504,12 @@ def main():
         "algorithmic_bytes_per_step": step.algo_bytes,
         "pct_hbm_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
         "cache_flush_between_steps": flush is not None,
-        "graph": "step replayed from one captured HIP graph",
+        "graph": "the step replayed from one captured HIP graph",
         "timed_wall_s": r["timed_wall_s"],
-        "sum_of_launches_us": r["sum_of_launches_us"],
+        "stage_us": r["stage_us"],
     }
     for key in ("dense_same_shape_us", "dense_same_shape_gbs", "dense_same_shape_pct_peak",
-                "quest_over_dense_time", "byte_model", "stage_us"):
+                "quest_over_dense_time", "byte_model"):
         if key in r:
             line[key] = r[key]
 
@@ -517,7 +529,6 @@ def main():
             "quest_us_per_step": q["us_per_step"],
             "quest_kv_gbs": round(q["gbs"], 1),
             "stage_us": q["stage_us"],
-            "sparse_attention_gbs": round(q["achieved"], 1),
             "dense_same_shape_us": q["dense_same_shape_us"],
             "dense_same_shape_gbs": q["dense_same_shape_gbs"],
             "dense_same_shape_pct_peak": q["dense_same_shape_pct_peak"],
