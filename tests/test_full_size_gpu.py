@@ -1,0 +1,198 @@
+"""GPU parity at the benchmark workloads' full sizes, in the launch
+configuration bench.py times (automatic split plan, default workspaces).
+
+The inputs come from the same seeded device generators as bench.py.  Outputs
+are compared with the fp64 oracle on sampled units the oracle computes one by
+one (a sequence, or a (batch, KV head) unit), with the bars of
+test_parity_gpu.py: attention max-abs <= 2e-3, metadata bit-exact, page
+scores within the fp32 accumulation bound, chosen pages identical up to
+near-ties.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import quest as oquest
+from decode_attention_folded_amd import workloads
+from test_parity_gpu import ATOL, check_selection, host, max_err, score_tolerance
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SEED = 2  # bench.py's default seed
+
+
+@pytest.fixture(scope="module")
+def da():
+    import decode_attention_folded_amd as pkg
+    pkg.load_library()
+    return pkg
+
+
+def f64(t):
+    return host(t).astype(np.float64)
+
+
+def test_full_gqa_layer(da):
+    """One layer: B=1, Hq=32, Hkv=8, D=64, 4096 valid keys; every output."""
+    c = workloads.device_dense(SEED, 1, 32, 8, 64, 4096, 4096, DEV)
+    out = da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"])
+    torch.cuda.synchronize()
+    want = oracle.decode_attention(host(c["q"]), host(c["k"]), host(c["v"]), [4096], 1 / 8.0)
+    assert max_err(f64(out), want) <= ATOL
+
+
+def test_full_exaone_30_layers(da):
+    """The 30-layer EXAONE-shaped step: every layer appends its row at slot
+    2999 and attends over 3000 keys of a 4096-slot cache; all 30 layers and
+    every output are checked, and the appended rows must be in the caches."""
+    layers, hq, hkv, d, cap, L = 30, 32, 8, 64, 4096, 3000
+    data = [workloads.device_dense(SEED * 100 + l, 1, hq, hkv, d, cap, L, DEV, with_new=True)
+            for l in range(layers)]
+    # host copies before the step writes slot L-1
+    before = [(host(c["k"]), host(c["v"])) for c in data]
+    ws = da.Workspace()
+    outs = []
+    for c in data:
+        outs.append(da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], k_new=c["k_new"],
+                                       v_new=c["v_new"], workspace=ws))
+    torch.cuda.synchronize()
+    for l, c in enumerate(data):
+        kn, vn = host(c["k_new"]), host(c["v_new"])
+        k2, v2 = oracle.append_kv(before[l][0], before[l][1], [L], kn, vn)
+        want = oracle.decode_attention(host(c["q"]), k2, v2, [L], 1 / 8.0)
+        assert max_err(f64(outs[l]), want) <= ATOL, l
+        assert np.array_equal(host(c["k"])[:, :, L - 1], kn[:, :])
+        assert np.array_equal(host(c["v"])[:, :, L - 1], vn[:, :])
+        # slots other than L-1 untouched
+        assert np.array_equal(host(c["k"])[:, :, :L - 1], before[l][0][:, :, :L - 1])
+
+
+def test_full_paged_batch64(da):
+    """Batched paged decode: B=64, Hq=32, Hkv=8, D=128, S=16, lengths
+    U[1024, 32768] over a permuted pool (the bench's grid: 8,192 workgroups).
+    Sampled sequences: the shortest, the longest and five more; every output
+    must be finite."""
+    b, hq, hkv, d, s, mp = 64, 32, 8, 128, 16, 2048
+    lens = workloads.draw_seqlens(3, b, 1024, 32768)
+    c = workloads.device_paged(SEED, b, hq, hkv, d, s, mp, lens, DEV)
+    out = da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], page_table=c["page_table"],
+                             page_size=s)
+    torch.cuda.synchronize()
+    got = f64(out)
+    assert np.all(np.isfinite(got))
+    table = c["page_table_host"]
+    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 13, 31, 47, 63})
+    for bi in picks:
+        n = (int(lens[bi]) + s - 1) // s
+        pages = torch.from_numpy(table[bi, :n].astype(np.int64)).to(DEV)
+        kc = host(c["k"][pages]).transpose(1, 0, 2, 3).reshape(1, hkv, n * s, d)
+        vc = host(c["v"][pages]).transpose(1, 0, 2, 3).reshape(1, hkv, n * s, d)
+        want = oracle.decode_attention(host(c["q"][bi:bi + 1]), kc, vc, [int(lens[bi])],
+                                       1 / math.sqrt(d))
+        assert max_err(got[bi:bi + 1], want) <= ATOL, (bi, int(lens[bi]))
+
+
+def _quest_unit_checks(q_unit, k_unit, meta_gpu_unit, scores_gpu_unit, idx_gpu_unit, L, s,
+                       k_pages, meta_want=None):
+    """Oracle checks of one (b, kv) unit: metadata bit-exact, scores within
+    the accumulation bound, selection under the near-tie rule, and sparse
+    attention over the GPU's own chosen pages."""
+    lens = [L]
+    n = oquest.page_count(L, s)
+    if meta_want is None:
+        meta_want = oquest.build_metadata(k_unit, lens, s, n)
+    assert np.array_equal(meta_gpu_unit[:, :, :n], meta_want[:, :, :n])
+    want_scores = oquest.page_scores(q_unit, meta_want, lens, s)
+    tol = score_tolerance(q_unit, meta_want, lens, s)
+    got_scores = scores_gpu_unit.astype(np.float64)
+    assert np.all(np.abs(got_scores[:, :, :n] - want_scores[:, :, :n]) <= tol[:, :, :n])
+    want_idx = oquest.select_pages(want_scores, lens, s, k_pages)
+    check_selection(idx_gpu_unit, got_scores, want_idx, want_scores, lens, s, k_pages)
+    return want_scores
+
+
+def test_full_quest_llama2_32k(da):
+    """Quest at the Llama2-7B shape: B=1, H=32, D=128, L=32768, S=16, budget
+    2048 (K=128), 8 planted pages per head.  Eight heads are checked: metadata,
+    scores, chosen pages, sparse attention; every sparse output finite."""
+    b, hq, hkv, d, L, s, budget = 1, 32, 32, 128, 32768, 16, 2048
+    c = workloads.device_dense(SEED, b, hq, hkv, d, L, L, DEV, plant_pages=8, plant_page_size=s)
+    P = L // s
+    meta = torch.zeros((b, hkv, P, 2, d), dtype=torch.float16, device=DEV)
+    da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], n_new=L, page_size=s)
+    scores = torch.empty((b, hkv, P), dtype=torch.float32, device=DEV)
+    idx = da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s, budget_tokens=budget,
+                                   page_scores=scores)
+    out = da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx,
+                                      budget_tokens=budget, page_size=s)
+    torch.cuda.synchronize()
+    got = f64(out)
+    assert np.all(np.isfinite(got))
+    meta_h, scores_h, idx_h = host(meta), host(scores), host(idx)
+    for h in (0, 5, 11, 16, 21, 26, 30, 31):
+        q_u = host(c["q"][:, h:h + 1])
+        k_u = host(c["k"][:, h:h + 1])
+        v_u = host(c["v"][:, h:h + 1])
+        _quest_unit_checks(q_u, k_u, meta_h[:, h:h + 1], scores_h[:, h:h + 1],
+                           idx_h[:, h:h + 1], L, s, budget // s)
+        want = oquest.sparse_decode_attention(q_u, k_u, v_u, [L], idx_h[:, h:h + 1], s,
+                                              1 / math.sqrt(d))
+        assert max_err(got[:, h:h + 1], want) <= ATOL, h
+
+
+def test_full_quest_gqa_128k_step(da):
+    """The long-context Quest GQA step: B=8, Hq=32, Hkv=8, D=128, L=131072,
+    S=16, budget 4096 (K=256), 16 planted pages per unit.  Metadata is built
+    in bulk, then the step appends one K/V row at slot 131071 with its
+    metadata update, scores and selects pages, and attends over them; dense
+    attention at the same shape (64 splits per unit) runs beside it.
+    Sampled units are checked against the oracle run through the same steps."""
+    b, hq, hkv, d, L, s, budget = 8, 32, 8, 128, 131072, 16, 4096
+    g = hq // hkv
+    c = workloads.device_dense(SEED, b, hq, hkv, d, L, L, DEV, plant_pages=16, plant_page_size=s,
+                               with_new=True)
+    P = L // s
+    meta = torch.zeros((b, hkv, P, 2, d), dtype=torch.float16, device=DEV)
+    da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], n_new=L, page_size=s)
+    units = [(0, 0), (3, 5), (7, 7), (5, 2)]
+    torch.cuda.synchronize()
+    k_before = {u: host(c["k"][u[0]:u[0] + 1, u[1]:u[1] + 1]) for u in units}
+    v_before = {u: host(c["v"][u[0]:u[0] + 1, u[1]:u[1] + 1]) for u in units}
+    # the step
+    da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], 1, page_size=s, k_new=c["k_new"],
+                         v_new=c["v_new"])
+    scores = torch.empty((b, hkv, P), dtype=torch.float32, device=DEV)
+    idx = da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s, budget_tokens=budget,
+                                   page_scores=scores)
+    out = da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx,
+                                      budget_tokens=budget, page_size=s)
+    dense = da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"])
+    torch.cuda.synchronize()
+    got, got_dense = f64(out), f64(dense)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_dense))
+    meta_h, scores_h, idx_h = host(meta), host(scores), host(idx)
+    kn_all, vn_all = host(c["k_new"]), host(c["v_new"])
+    for (bi, kv) in units:
+        q_u = host(c["q"][bi:bi + 1, kv * g:(kv + 1) * g])
+        kn = kn_all[bi:bi + 1, kv:kv + 1]
+        vn = vn_all[bi:bi + 1, kv:kv + 1]
+        k_u, v_u = oracle.append_kv(k_before[(bi, kv)], v_before[(bi, kv)], [L], kn, vn)
+        # the cache now holds the appended row
+        assert np.array_equal(host(c["k"][bi, kv, L - 1]), kn[0, 0])
+        assert np.array_equal(host(c["v"][bi, kv, L - 1]), vn[0, 0])
+        meta_want = oquest.build_metadata(k_before[(bi, kv)], [L], s, P)
+        meta_want = oquest.append_metadata(meta_want, k_u, [L], 1, s)
+        _quest_unit_checks(q_u, k_u, meta_h[bi:bi + 1, kv:kv + 1],
+                           scores_h[bi:bi + 1, kv:kv + 1], idx_h[bi:bi + 1, kv:kv + 1],
+                           L, s, budget // s, meta_want=meta_want)
+        rows = slice(kv * g, (kv + 1) * g)
+        want = oquest.sparse_decode_attention(q_u, k_u, v_u, [L], idx_h[bi:bi + 1, kv:kv + 1], s,
+                                              1 / math.sqrt(d))
+        assert max_err(got[bi:bi + 1, rows], want) <= ATOL, (bi, kv)
+        want_dense = oracle.decode_attention(q_u, k_u, v_u, [L], 1 / math.sqrt(d))
+        assert max_err(got_dense[bi:bi + 1, rows], want_dense) <= ATOL, (bi, kv)
