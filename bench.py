@@ -57,7 +57,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="exaone30",
-                    choices=["exaone30", "gqa1", "paged", "quest32k", "quest128k"])
+                    choices=["exaone30", "gqa1", "paged", "quest32k", "quest128k",
+                             "repeat_kv_ab"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true",
@@ -433,6 +434,77 @@ def measure(torch, da, dev, step, steps, warmup, flush):
     return res
 
 
+def repeat_kv_ab(da, torch, seed, dev, steps, warmup, flush):
+    """The fold against the materialised repeat_kv path ([CoreML-GQA] section
+    4's comparison) at the single-layer, 30-layer EXAONE-shaped and batched
+    paged shapes.  Materialised = gqa_repeat_kv (each KV head copied to its G
+    query heads) + the same attention kernel at G = 1.  Both sides read the
+    same valid rows and skip the append (the materialised side has no
+    separate append path)."""
+    from decode_attention_folded_amd import workloads
+    import numpy as np
+
+    def timed(fns, reps):
+        g = capture(torch, fns)
+        return statistics.median(time_stages(torch, [g], reps, 2, flush)[0]) * 1e3
+
+    out = {}
+    cases = []
+    # single layer and the 30-layer step (B=1, Hq=32, Hkv=8, D=64)
+    for name, layers, L, cap in (("gqa_layer_ctx4096", 1, 4096, 4096),
+                                 ("exaone_30_layers_len3000", 30, 3000, 4096)):
+        data = [workloads.device_dense(seed * 100 + l, 1, 32, 8, 64, cap, L, dev)
+                for l in range(layers)]
+        for c in data:
+            c["kr"] = torch.empty((1, 32, cap, 64), dtype=torch.float16, device=dev)
+            c["vr"] = torch.empty_like(c["kr"])
+            c["out"] = torch.empty_like(c["q"])
+        kv_bytes = layers * 2 * 8 * L * 64 * 2
+        cases.append((name, data, None, 16, kv_bytes, 4))
+    # batched paged decode (B=64, Hq=32, Hkv=8, D=128, S=16, U[1K, 32K])
+    lens = workloads.draw_seqlens(3, 64, 1024, 32768)
+    pc = workloads.device_paged(seed, 64, 32, 8, 128, 16, 2048, lens, dev)
+    pc["kr"] = torch.empty((64, 32, 2048 * 16, 128), dtype=torch.float16, device=dev)
+    pc["vr"] = torch.empty_like(pc["kr"])
+    pc["out"] = torch.empty_like(pc["q"])
+    cases.append(("paged_b64_len1k-32k", [pc], pc["page_table"], 16,
+                  int(2 * 8 * 128 * 2 * int(np.sum(lens))), 4))
+    for name, data, table, s, kv_bytes, g in cases:
+        ws = da.Workspace(dev)
+        fold = [lambda c=c: da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"],
+                                               page_table=table, page_size=s, out=c["out"],
+                                               workspace=ws) for c in data]
+        copy = [lambda c=c: da.gqa_repeat_kv(c["k"], c["v"], c["seqlens"], 32, page_table=table,
+                                             page_size=s, k_out=c["kr"], v_out=c["vr"])
+                for c in data]
+        attn1 = [lambda c=c: da.gqa_decode_attn(c["q"], c["kr"], c["vr"], c["seqlens"],
+                                                out=c["out"], workspace=ws) for c in data]
+        for f in fold + copy + attn1:
+            f()
+        torch.cuda.synchronize()
+        reps = max(5, steps // 2) if name.startswith("paged") else steps
+        t_fold = timed(fold, reps)
+        t_copy = timed(copy, reps)
+        t_attn1 = timed(attn1, reps)
+        t_both = timed(copy + attn1, reps)
+        out[name] = {
+            "fold_us": round(t_fold, 3),
+            "materialised_us": round(t_both, 3),
+            "repeat_kv_copy_us": round(t_copy, 3),
+            "attention_g1_us": round(t_attn1, 3),
+            "materialised_over_fold": round(t_both / t_fold, 3),
+            "kv_bytes": kv_bytes,
+            "copy_bytes": kv_bytes * (1 + g),
+            "copy_gbs": round(kv_bytes * (1 + g) / (t_copy * 1e-6) / 1e9, 1),
+            "byte_model_materialised_over_fold": 1 + 2 * g,
+        }
+        for c in data:
+            del c["kr"], c["vr"]
+        del data
+        torch.cuda.empty_cache()
+    return out
+
+
 MAKERS = {
     "exaone30": exaone30, "gqa1": gqa1, "paged": paged,
     "quest32k": lambda *a: quest(*a, long_ctx=False),
@@ -453,6 +525,31 @@ def main():
     torch.cuda.set_device(dev)
     flush = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
+    if args.workload == "repeat_kv_ab":
+        ab = repeat_kv_ab(da, torch, args.seed, dev, args.steps, args.warmup, flush)
+        ex = ab["exaone_30_layers_len3000"]
+        big = ab["paged_b64_len1k-32k"]
+        line = {
+            "metric": "fold vs materialised repeat_kv (copy + G=1 attention): time ratio",
+            "value": ex["materialised_over_fold"], "unit": "x", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ex["fold_us"] * 1e-3, 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16 in, f32 accumulate",
+            "data": "synthetic N(0,1) fp16, seeded",
+            "config": {"workload": "repeat_kv_ab: gqa layer, exaone 30 layers, paged b64"},
+            "roofline": {"bound": "hbm", "achieved": big["copy_gbs"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(big["copy_gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel": "repeat_kv_kernel (gqa_repeat_kv)",
+                         "stage": "repeat_kv copy, paged b64",
+                         "bytes_per_call": big["copy_bytes"],
+                         "us_per_call": big["repeat_kv_copy_us"],
+                         "time_source": "HIP events around replays of the call's graph after "
+                                        "a cache flush (median)"},
+            "repeat_kv_ab": ab,
+            "cache_flush_between_steps": flush is not None,
+        }
+        print(json.dumps(line), flush=True)
+        return 0
     step, data = MAKERS[args.workload](da, torch, args.seed, dev)
     r = measure(torch, da, dev, step, args.steps, args.warmup, flush)
 

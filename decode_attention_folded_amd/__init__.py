@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
 * :func:`quest_meta_append`        -- per-page Key min/max metadata update
 * :func:`quest_page_score_topk`    -- page scores and top-K page selection
 * :func:`quest_sparse_decode_attn` -- attention over the selected pages
+* :func:`gqa_repeat_kv`            -- the materialised repeat_kv copy (A/B baseline)
 """
 
 _EXPORTS = (
@@ -19,6 +20,7 @@ _EXPORTS = (
     "quest_meta_append",
     "quest_page_score_topk",
     "quest_sparse_decode_attn",
+    "gqa_repeat_kv",
     "workspace_bytes",
     "quest_workspace_bytes",
     "Workspace",

@@ -28,6 +28,7 @@ STATUS_NAMES = {
 EXPORTED_SYMBOLS = (
     "da_status_string", "da_workspace_size", "gqa_decode_attn", "quest_meta_append",
     "da_quest_workspace_size", "quest_page_score_topk", "quest_sparse_decode_attn",
+    "gqa_repeat_kv",
 )
 
 
@@ -245,6 +246,30 @@ def gqa_decode_attn(q, k_cache, v_cache, seqlens, *, scale=None, k_new=None, v_n
                                num_splits, _stream_handle(q.device, stream)),
            "gqa_decode_attn")
     return out
+
+
+def gqa_repeat_kv(k_cache, v_cache, seqlens, num_q_heads, *, page_table=None, page_size=0,
+                  k_out=None, v_out=None, stream=None):
+    """Materialised repeat_kv (see ``gqa_repeat_kv`` in decode_attn.h): returns
+    k_out, v_out [B, Hq, cap, D] fp16 whose rows t < L_b of head h are the rows
+    of KV head h // G (other rows are left as allocated)."""
+    lib = load_library()
+    _need(seqlens, "seqlens", torch.int32, 1)
+    batch = seqlens.shape[0]
+    desc = _kv_desc(k_cache, v_cache, batch, page_table, page_size)
+    shape = (batch, int(num_q_heads), desc.capacity, desc.head_dim)
+    outs = []
+    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float16, device=k_cache.device)
+        _need(t, name, torch.float16, 4)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be [B, Hq, cap, D] = {shape}")
+        outs.append(t)
+    _check(lib.gqa_repeat_kv(ctypes.byref(desc), int(num_q_heads), _ptr(seqlens), _ptr(outs[0]),
+                             _ptr(outs[1]), _stream_handle(k_cache.device, stream)),
+           "gqa_repeat_kv")
+    return outs[0], outs[1]
 
 
 def quest_meta_append(k_cache, v_cache, meta, seqlens, n_new=1, *, page_size, k_new=None,

@@ -246,6 +246,40 @@ int quest_sparse_decode_attn(const void* q, const da_kv_cache* kv, const int32_t
                        nullptr, out, workspace, workspace_bytes, num_splits, stream);
 }
 
+int gqa_repeat_kv(const da_kv_cache* kv, int32_t num_q_heads, const int32_t* seqlens,
+                  void* k_out, void* v_out, void* stream) {
+  Shape s;
+  int st = check_cache(kv, num_q_heads, &s);
+  if (st != DA_OK) return st;
+  if (s.paged && !is_pow2_in(s.page_size, 8, 64)) return DA_ERR_UNSUPPORTED;
+  const int64_t rows = da::repeat_kv_rows_per_workgroup();
+  if ((s.capacity + rows - 1) / rows * s.batch * s.hkv > INT32_MAX) return DA_ERR_SHAPE;
+  if (s.batch == 0) return DA_OK;  // nothing to read or write
+  if (seqlens == nullptr || kv->k == nullptr || kv->v == nullptr || k_out == nullptr ||
+      v_out == nullptr)
+    return DA_ERR_NULL;
+  if (!aligned16(kv->k) || !aligned16(kv->v) || !aligned16(k_out) || !aligned16(v_out))
+    return DA_ERR_SHAPE;
+  da::RepeatLaunch a;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_table = kv->page_table;
+  a.seqlens = seqlens;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.batch = s.batch;
+  a.num_kv_heads = s.hkv;
+  a.group = s.group;
+  a.head_dim = s.d;
+  a.capacity = s.capacity;
+  a.cache_stride = s.stride;
+  a.page_shift = s.paged ? log2i(s.page_size) : 0;
+  a.max_pages = s.max_pages;
+  a.num_pages = kv->num_pages;
+  a.out_capacity = s.capacity;
+  return da::launch_repeat_kv(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
+}
+
 int quest_meta_append(const da_kv_cache* kv, void* meta, int32_t meta_max_pages,
                       const int32_t* seqlens, int32_t n_new, const void* k_new,
                       const void* v_new, void* stream) {

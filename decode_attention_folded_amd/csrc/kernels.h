@@ -80,4 +80,21 @@ struct ScoreLaunch {
 int launch_score_topk(const ScoreLaunch& p, void* stream);
 int topk_max_pages();
 
+// Materialised repeat_kv: rows t < L_b of every KV head copied to its G query
+// heads, out [B, Hq, out_capacity, D].
+struct RepeatLaunch {
+  const void* k;             // cache or pool
+  const void* v;
+  const int32_t* page_table;
+  const int32_t* seqlens;
+  void* k_out;               // fp16 [B, Hq, out_capacity, D]
+  void* v_out;
+  int32_t batch, num_kv_heads, group, head_dim;
+  int32_t capacity, cache_stride, page_shift, max_pages;
+  int64_t num_pages;
+  int32_t out_capacity;
+};
+int launch_repeat_kv(const RepeatLaunch& p, void* stream);
+int repeat_kv_rows_per_workgroup();
+
 }  // namespace da

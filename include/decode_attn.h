@@ -121,6 +121,27 @@ int gqa_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens
                     void* stream);
 
 /*
+ * Materialised repeat_kv, the copy the fold removes; for A/B comparison only.
+ * [CoreML-GQA] section 2 "Why Does GQA Replicate KV?" (and "expand Is a View,
+ * but reshape Introduces a Copy"): the GQA reference path copies each KV head
+ * to the G query heads that read it.  This call builds that tensor so that
+ * gqa_decode_attn can run on it with num_kv_heads = Hq (G = 1), the baseline
+ * of the page's section 4 comparison.
+ *
+ *   kv         (host)   cache description (contiguous or paged)
+ *   num_q_heads Hq; G = Hq / Hkv in {1, 2, 4, 8}
+ *   seqlens    (device) int32 [B]; clamped to [0, capacity] on the device
+ *   k_out, v_out (device) fp16 [B, Hq, cap, D], cap = kv->capacity (contiguous)
+ *              or kv->max_pages * page_size (paged): row t of head h is row t
+ *              of KV head h / G for t < L_b.  Rows t >= L_b, and rows of a
+ *              paged sequence whose page-table entry is outside the pool, are
+ *              not written.  The outputs must not overlap the cache.
+ * Reads every valid cache byte once and writes it G times.
+ */
+int gqa_repeat_kv(const da_kv_cache* kv, int32_t num_q_heads, const int32_t* seqlens,
+                  void* k_out, void* v_out, void* stream);
+
+/*
  * Quest metadata update.  [Quest-review] "the page score is not an exact
  * attention probability" (paper section 3.4): per page p and channel i keep
  * the Key minimum m_{p,i} and maximum M_{p,i}, updated as new Keys arrive.

@@ -124,6 +124,18 @@ def test_quest_validation_codes(lib):
     assert st == -3
 
 
+def test_repeat_kv_validation_codes(lib):
+    P = ctypes.c_void_p
+    d = _desc()
+    assert lib.gqa_repeat_kv(ctypes.byref(d), 32, P(FAKE), None, P(FAKE), None) == -1
+    assert lib.gqa_repeat_kv(ctypes.byref(d), 32, None, P(FAKE), P(FAKE), None) == -1
+    assert lib.gqa_repeat_kv(ctypes.byref(d), 8 * 16, P(FAKE), P(FAKE), P(FAKE), None) == -3
+    assert lib.gqa_repeat_kv(ctypes.byref(d), 30, P(FAKE), P(FAKE), P(FAKE), None) == -2
+    assert lib.gqa_repeat_kv(ctypes.byref(d), 32, P(FAKE), P(FAKE + 4), P(FAKE), None) == -2
+    assert lib.gqa_repeat_kv(ctypes.byref(_desc(batch=0)), 32, None, None, None, None) == 0
+    assert lib.gqa_repeat_kv(None, 32, P(FAKE), P(FAKE), P(FAKE), None) == -1
+
+
 def test_workspace_sizes(lib):
     def size(desc, hq=32, budget=0, splits=0):
         out = ctypes.c_size_t()

@@ -429,6 +429,49 @@ def test_quest_pipeline_end_to_end(da):
         assert max_err(host(out), want) <= ATOL
 
 
+# ------------------------------------------------------------ repeat_kv A/B
+
+
+@pytest.mark.parametrize("d,g,cap,lens", [(64, 4, 700, [700, 129, 1]), (128, 8, 300, [300, 65]),
+                                          (128, 1, 200, [200, 0])])
+def test_repeat_kv_copy_and_g1_attention(da, d, g, cap, lens):
+    """The materialised copy equals the oracle's repeat_kv on every valid row
+    (bit-exact), leaves rows past L_b untouched, and attention on it at G = 1
+    matches the oracle and the folded kernel."""
+    hkv = 2
+    case = workloads.dense_case(810 + g, len(lens), hkv * g, hkv, d, cap, lens)
+    k, v, sl = dev(case.k), dev(case.v), dev(case.seqlens)
+    sentinel = torch.full((len(lens), hkv * g, cap, d), 7.0, dtype=torch.float16, device=DEV)
+    kr, vr = da.gqa_repeat_kv(k, v, sl, hkv * g, k_out=sentinel.clone(), v_out=sentinel.clone())
+    torch.cuda.synchronize()
+    want_k, want_v = oracle.repeat_kv(case.k, g), oracle.repeat_kv(case.v, g)
+    kr_h, vr_h = host(kr), host(vr)
+    for b, lb in enumerate(lens):
+        assert np.array_equal(kr_h[b, :, :lb], want_k[b, :, :lb])
+        assert np.array_equal(vr_h[b, :, :lb], want_v[b, :, :lb])
+        assert np.all(kr_h[b, :, lb:] == 7.0) and np.all(vr_h[b, :, lb:] == 7.0)
+    out_g1 = host(da.gqa_decode_attn(dev(case.q), kr, vr, sl)).astype(np.float64)
+    out_fold = host(da.gqa_decode_attn(dev(case.q), k, v, sl)).astype(np.float64)
+    want = oracle.decode_attention(case.q, case.k, case.v, case.seqlens, case.scale)
+    assert max_err(out_g1, want) <= ATOL
+    assert max_err(out_fold, want) <= ATOL
+
+
+def test_repeat_kv_from_paged_cache(da):
+    """A paged pool is materialised into the contiguous [B, Hq, cap, D] layout."""
+    case = workloads.paged_case(820, 3, 16, 4, 64, 16, 40, [640, 17, 300])
+    k, v = dev(case.k), dev(case.v)
+    kr, vr = da.gqa_repeat_kv(k, v, dev(case.seqlens), 16, page_table=dev(case.page_table),
+                              page_size=16)
+    torch.cuda.synchronize()
+    kc = oracle.gather_paged(case.k, case.page_table, 16, 40 * 16)
+    vc = oracle.gather_paged(case.v, case.page_table, 16, 40 * 16)
+    want_k, want_v = oracle.repeat_kv(kc, 4), oracle.repeat_kv(vc, 4)
+    for b, lb in enumerate(case.seqlens):
+        assert np.array_equal(host(kr)[b, :, :lb], want_k[b, :, :lb])
+        assert np.array_equal(host(vr)[b, :, :lb], want_v[b, :, :lb])
+
+
 def test_split_merge_reads_fresh_partials(da):
     """Calls alternate between different inputs and split counts on one
     workspace: every merge must see this call's partials, never the previous
