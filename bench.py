@@ -183,6 +183,11 @@ def quest(da, torch, seed, dev, long_ctx):
         da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], 1, page_size=s,
                              k_new=c["k_new"], v_new=c["v_new"])
 
+    def append_select():   # the step's append fused into the score launch
+        da.quest_append_score_topk(c["q"], c["k"], c["v"], meta, c["seqlens"], c["k_new"],
+                                   c["v_new"], page_size=s, budget_tokens=budget,
+                                   page_idx=idx, page_scores=scores)
+
     def select():
         da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s, budget_tokens=budget,
                                  page_idx=idx, page_scores=scores)
@@ -205,17 +210,22 @@ def quest(da, torch, seed, dev, long_ctx):
     # append: the new K/V row (read + write) and the touched page's min/max
     append_bytes = units * (2 * 2 * d * 2 + 2 * 2 * d * 2)
     algo = score_bytes + attend_bytes + (append_bytes if long_ctx else 0)
-    stages = ([Stage("meta_append", [append], append_bytes, "meta_append_kernel")]
-              if long_ctx else [])
-    stages += [Stage("score_topk", [select], score_bytes,
-                     "page_score_kernel + topk_kernel (quest_page_score_topk)"),
-               Stage("sparse_attention", [attend], attend_bytes,
-                     "decode_kernel + merge_kernel (quest_sparse_decode_attn)")]
+    if long_ctx:
+        stages = [Stage("append_score_topk", [append_select], score_bytes + append_bytes,
+                        "page_score_kernel (with the append) + topk_kernel "
+                        "(quest_append_score_topk)")]
+    else:
+        stages = [Stage("score_topk", [select], score_bytes,
+                        "page_score_kernel + topk_kernel (quest_page_score_topk)")]
+    stages.append(Stage("sparse_attention", [attend], attend_bytes,
+                        "decode_kernel + merge_kernel (quest_sparse_decode_attn)"))
     cfg = {"workload": name, "batch": b, "num_q_heads": hq, "num_kv_heads": hkv,
            "head_dim": d, "seq_len": L, "page_size": s, "budget_tokens": budget,
            "k_pages": k_sel}
     st = Step("quest128k" if long_ctx else "quest32k", cfg, kv_bytes, algo, stages)
     st.dense_fn = dense
+    if long_ctx:   # the same step with the append as its own launch, for comparison
+        st.separate_append_fns = [append, select, attend]
     st.dense_bytes = dense_bytes
     st.byte_model = {"meta_bytes": meta_bytes, "selected_bytes": sel_bytes,
                      "dense_bytes": dense_bytes,
@@ -422,6 +432,10 @@ def measure(torch, da, dev, step, steps, warmup, flush):
         "timed_wall_s": round(t_wall, 3),
         "stage_us": {st.name: round(m * 1e3, 3) for st, m in zip(step.stages, med)},
     }
+    if hasattr(step, "separate_append_fns"):
+        g = capture(torch, step.separate_append_fns)
+        sep_ms = statistics.median(time_stages(torch, [g], steps, 2, flush)[0])
+        res["step_us_separate_append"] = round(sep_ms * 1e3, 3)
     if hasattr(step, "dense_fn"):
         g = capture(torch, [step.dense_fn])
         dense_ms = statistics.median(time_stages(torch, [g], max(10, steps // 2), 2, flush)[0])
@@ -606,7 +620,7 @@ def main():
         "stage_us": r["stage_us"],
     }
     for key in ("dense_same_shape_us", "dense_same_shape_gbs", "dense_same_shape_pct_peak",
-                "quest_over_dense_time", "byte_model"):
+                "quest_over_dense_time", "byte_model", "step_us_separate_append"):
         if key in r:
             line[key] = r[key]
 
@@ -624,6 +638,7 @@ def main():
         line["long_context"] = {
             "workload": qstep.config["workload"],
             "quest_us_per_step": q["us_per_step"],
+            "quest_us_per_step_separate_append": q["step_us_separate_append"],
             "quest_kv_gbs": round(q["gbs"], 1),
             "stage_us": q["stage_us"],
             "dense_same_shape_us": q["dense_same_shape_us"],

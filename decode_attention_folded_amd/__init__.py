@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
 * :func:`gqa_decode_attn`          -- folded decode attention, dense or paged
 * :func:`quest_meta_append`        -- per-page Key min/max metadata update
 * :func:`quest_page_score_topk`    -- page scores and top-K page selection
+* :func:`quest_append_score_topk`  -- the step's append fused into scoring + top-K
 * :func:`quest_sparse_decode_attn` -- attention over the selected pages
 * :func:`gqa_repeat_kv`            -- the materialised repeat_kv copy (A/B baseline)
 """
@@ -19,6 +20,7 @@ _EXPORTS = (
     "gqa_decode_attn",
     "quest_meta_append",
     "quest_page_score_topk",
+    "quest_append_score_topk",
     "quest_sparse_decode_attn",
     "gqa_repeat_kv",
     "workspace_bytes",

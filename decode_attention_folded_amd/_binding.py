@@ -28,7 +28,7 @@ STATUS_NAMES = {
 EXPORTED_SYMBOLS = (
     "da_status_string", "da_workspace_size", "gqa_decode_attn", "quest_meta_append",
     "da_quest_workspace_size", "quest_page_score_topk", "quest_sparse_decode_attn",
-    "gqa_repeat_kv",
+    "gqa_repeat_kv", "quest_append_score_topk",
 )
 
 
@@ -330,6 +330,51 @@ def quest_page_score_topk(q, meta, seqlens, *, page_size, budget_tokens, page_id
                                      _ptr(page_scores), _ptr(ws), 0 if ws is None else ws.numel(),
                                      _stream_handle(q.device, stream)),
            "quest_page_score_topk")
+    return page_idx
+
+
+def quest_append_score_topk(q, k_cache, v_cache, meta, seqlens, k_new, v_new, *, page_size,
+                            budget_tokens, page_table=None, page_idx=None, page_scores=None,
+                            workspace=None, stream=None):
+    """One decode step's K/V row append and metadata update fused into page
+    scoring and top-K (see ``quest_append_score_topk`` in decode_attn.h).
+    Updates the cache and meta in place; returns page_idx [B, Hkv, K] int32."""
+    lib = load_library()
+    _need(q, "q", torch.float16, 3)
+    _need(meta, "meta", torch.float16, 5)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    batch, hq, d = q.shape
+    desc = _kv_desc(k_cache, v_cache, batch, page_table, page_size)
+    _check_common(q, seqlens, desc)
+    if tuple(meta.shape) != (batch, desc.num_kv_heads, meta.shape[2], 2, d):
+        raise ValueError("meta must be [B, Hkv, P, 2, D]")
+    _need(k_new, "k_new", torch.float16, 3)
+    _need(v_new, "v_new", torch.float16, 3)
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if tuple(t.shape) != (batch, desc.num_kv_heads, d):
+            raise ValueError(f"{name} must be [B, Hkv, D]")
+    hkv, max_pages = desc.num_kv_heads, meta.shape[2]
+    k_pages = int(budget_tokens) // int(page_size) if page_size > 0 else 0
+    if page_idx is None:
+        page_idx = torch.empty((batch, hkv, max(k_pages, 1)), dtype=torch.int32, device=q.device)
+    else:
+        _need(page_idx, "page_idx", torch.int32, 3)
+        if tuple(page_idx.shape) != (batch, hkv, k_pages):
+            raise ValueError("page_idx must be [B, Hkv, budget_tokens / page_size]")
+    ws = None
+    if page_scores is None:
+        ws = _workspace(workspace, q.device, "scores").get(
+            quest_workspace_bytes(batch, hkv, max_pages), q.device)
+    else:
+        _need(page_scores, "page_scores", torch.float32, 3)
+        if tuple(page_scores.shape) != (batch, hkv, max_pages):
+            raise ValueError("page_scores must be [B, Hkv, P]")
+    _check(lib.quest_append_score_topk(_ptr(q), ctypes.byref(desc), _ptr(meta), max_pages,
+                                       _ptr(seqlens), hq, int(budget_tokens), _ptr(k_new),
+                                       _ptr(v_new), _ptr(page_idx), _ptr(page_scores), _ptr(ws),
+                                       0 if ws is None else ws.numel(),
+                                       _stream_handle(q.device, stream)),
+           "quest_append_score_topk")
     return page_idx
 
 

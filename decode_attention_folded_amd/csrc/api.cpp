@@ -364,7 +364,7 @@ int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_page
   }
   da::ScoreLaunch a;
   a.q = q;
-  a.meta = meta;
+  a.meta = const_cast<void*>(meta);  // read only: no append on this path
   a.seqlens = seqlens;
   a.scores = scores;
   a.page_idx = page_idx;
@@ -375,6 +375,69 @@ int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_page
   a.page_shift = log2i(page_size);
   a.meta_max_pages = meta_max_pages;
   a.num_sel = budget_tokens / page_size;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.k = nullptr;
+  a.v = nullptr;
+  a.page_table = nullptr;
+  a.capacity = 0;
+  a.cache_stride = 0;
+  a.max_pages = 0;
+  a.num_pages = 0;
+  return da::launch_score_topk(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
+}
+
+int quest_append_score_topk(const void* q, const da_kv_cache* kv, void* meta,
+                            int32_t meta_max_pages, const int32_t* seqlens, int32_t num_q_heads,
+                            int32_t budget_tokens, const void* k_new, const void* v_new,
+                            int32_t* page_idx, float* page_scores, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  Shape s;
+  int st = check_cache(kv, num_q_heads, &s);
+  if (st != DA_OK) return st;
+  if (!is_pow2_in(s.page_size, 8, 64)) return DA_ERR_UNSUPPORTED;
+  if (budget_tokens <= 0 || budget_tokens % s.page_size != 0) return DA_ERR_BUDGET;
+  if (meta_max_pages < 1 || (int64_t)meta_max_pages * s.page_size < s.capacity)
+    return DA_ERR_SHAPE;
+  if (meta_max_pages > da::topk_max_pages()) return DA_ERR_UNSUPPORTED;
+  if (s.batch == 0) return DA_OK;  // nothing to read or write
+  if (q == nullptr || meta == nullptr || seqlens == nullptr || page_idx == nullptr ||
+      k_new == nullptr || v_new == nullptr || kv->k == nullptr || kv->v == nullptr)
+    return DA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(meta) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned16(kv->k) || !aligned16(kv->v))
+    return DA_ERR_SHAPE;
+  float* scores = page_scores;
+  if (scores == nullptr) {
+    size_t need = 0;
+    da_quest_workspace_size(s.batch, s.hkv, meta_max_pages, &need);
+    if (workspace == nullptr) return DA_ERR_NULL;
+    if (!aligned16(workspace)) return DA_ERR_SHAPE;
+    if (workspace_bytes < need) return DA_ERR_WORKSPACE;
+    scores = static_cast<float*>(workspace);
+  }
+  da::ScoreLaunch a;
+  a.q = q;
+  a.meta = meta;
+  a.seqlens = seqlens;
+  a.scores = scores;
+  a.page_idx = page_idx;
+  a.batch = s.batch;
+  a.num_kv_heads = s.hkv;
+  a.group = s.group;
+  a.head_dim = s.d;
+  a.page_shift = log2i(s.page_size);
+  a.meta_max_pages = meta_max_pages;
+  a.num_sel = budget_tokens / s.page_size;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_table = kv->page_table;
+  a.capacity = s.capacity;
+  a.cache_stride = s.stride;
+  a.max_pages = s.max_pages;
+  a.num_pages = kv->num_pages;
   return da::launch_score_topk(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
 }
 

@@ -69,13 +69,23 @@ int launch_meta_append(const MetaLaunch& p, void* stream);
 
 struct ScoreLaunch {
   const void* q;             // fp16 [B, Hq, D]
-  const void* meta;          // fp16 [B, Hkv, P, 2, D]
+  void* meta;                // fp16 [B, Hkv, P, 2, D]; written only with k_new
   const int32_t* seqlens;
   float* scores;             // [B, Hkv, P]
   int32_t* page_idx;         // [B, Hkv, K]
   int32_t batch, num_kv_heads, group, head_dim;
   int32_t page_shift, meta_max_pages, num_sel;
   int32_t score_passes;      // set by the launcher
+  // Fused decode-step append (k_new != nullptr): row min(L_b, capacity) - 1 of
+  // the cache receives k_new / v_new and its page's metadata is updated (reset
+  // at a page start, min/max otherwise) before the page is scored.
+  const void* k_new;         // fp16 [B, Hkv, D] or nullptr
+  const void* v_new;
+  void* k;                   // cache or pool (written only with k_new)
+  void* v;
+  const int32_t* page_table; // [B, max_pages] or nullptr (contiguous cache)
+  int32_t capacity, cache_stride, max_pages;
+  int64_t num_pages;
 };
 int launch_score_topk(const ScoreLaunch& p, void* stream);
 int topk_max_pages();

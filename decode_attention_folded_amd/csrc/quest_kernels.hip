@@ -156,7 +156,24 @@ __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLa
     }
   }
 
-  const f16* mbase = reinterpret_cast<const f16*>(a.meta) + unit * a.meta_max_pages * 2 * D;
+  // Fused append: the page holding the step's new key, its new min/max chunk.
+  int p_app = -1;  // no lane matches when there is no append
+  bool fresh = false;
+  f16x8 knew = {}, vnew = {};
+  int t_app = 0;
+  if (a.k_new != nullptr) {
+    int La = a.seqlens[b];
+    La = La < 0 ? 0 : (La > a.capacity ? a.capacity : La);
+    if (La >= 1) {
+      t_app = La - 1;
+      p_app = t_app >> shift;
+      fresh = (t_app & ((1 << shift) - 1)) == 0;
+      knew = *reinterpret_cast<const f16x8*>(reinterpret_cast<const f16*>(a.k_new) + unit * D + 8 * ch);
+      vnew = *reinterpret_cast<const f16x8*>(reinterpret_cast<const f16*>(a.v_new) + unit * D + 8 * ch);
+    }
+  }
+
+  f16* mbase = reinterpret_cast<f16*>(a.meta) + unit * a.meta_max_pages * 2 * D;
   float* scores = a.scores + unit * a.meta_max_pages;
   for (int pass = 0; pass < a.score_passes; ++pass) {
     const int p0 = wg_begin + pass * SS::PAGES_PER_PASS;
@@ -171,6 +188,18 @@ __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLa
       mins[u] = stream_load(mbase + pp * 2 * D + 8 * ch);
       maxs[u] = stream_load(mbase + pp * 2 * D + D + 8 * ch);
     }
+    // the appended key enters its page's min/max before the page is scored
+    // (selects, no branch: the wait counts of the loads stay exact)
+    int app_u = -1;
+#pragma unroll
+    for (int u = 0; u < kScoreDepth; ++u) {
+      const bool hit = pg[u] == p_app;
+      app_u = hit ? u : app_u;
+      const f16x8 mn = fresh ? knew : __builtin_elementwise_min(mins[u], knew);
+      const f16x8 mx = fresh ? knew : __builtin_elementwise_max(maxs[u], knew);
+      mins[u] = hit ? mn : mins[u];
+      maxs[u] = hit ? mx : maxs[u];
+    }
 #pragma unroll
     for (int u = 0; u < kScoreDepth; ++u) {
       float s = 0.0f;
@@ -181,6 +210,30 @@ __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLa
       }
       s = group_sum<LPP>(s);
       if (ch == 0 && pg[u] < n_pages) scores[pg[u]] = s;
+    }
+    if (app_u >= 0) {  // the D/8 lanes of the appended page write its row back
+      f16x8 mn = mins[0], mx = maxs[0];
+#pragma unroll
+      for (int u = 1; u < kScoreDepth; ++u) {
+        mn = app_u == u ? mins[u] : mn;
+        mx = app_u == u ? maxs[u] : mx;
+      }
+      f16* mrow = mbase + (int64_t)p_app * 2 * D + 8 * ch;
+      *reinterpret_cast<f16x8*>(mrow) = mn;
+      *reinterpret_cast<f16x8*>(mrow + D) = mx;
+      int64_t off = -1;
+      if (a.page_table != nullptr) {
+        const int phys = p_app < a.max_pages ? a.page_table[(int64_t)b * a.max_pages + p_app] : -1;
+        if (phys >= 0 && phys < a.num_pages)
+          off = (((int64_t)phys * a.num_kv_heads + kv) << shift) * D +
+                (int64_t)(t_app & ((1 << shift) - 1)) * D;
+      } else {
+        off = (unit * a.cache_stride + t_app) * D;
+      }
+      if (off >= 0) {
+        *reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(a.k) + off + 8 * ch) = knew;
+        *reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(a.v) + off + 8 * ch) = vnew;
+      }
     }
   }
 }

@@ -199,6 +199,35 @@ int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_page
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step's cache and metadata update fused into page scoring:
+ * the effect of quest_meta_append(kv, meta, meta_max_pages, seqlens, 1, k_new,
+ * v_new) followed by quest_page_score_topk(q, meta, ...) in one score launch
+ * plus the top-K launch, with bit-identical results.  [Quest-review] (paper
+ * section 3.4): the metadata is updated as each new Key arrives, then the
+ * query scores the pages; [CoreML-GQA] section 5 names the update path as the
+ * next thing to fuse.  The workgroup that scores page (L_b - 1) / S folds
+ * k_new into that page's min/max (reset at a page start) before scoring it,
+ * writes the page's metadata back and stores k_new / v_new at slot L_b - 1 of
+ * the cache.
+ *
+ *   q          (device) fp16 [B, Hq, D]
+ *   kv         (host)   cache description (contiguous or paged); S =
+ *              kv->page_size in {8, 16, 32, 64}; D and Hkv from kv
+ *   meta       (device) fp16 [B, Hkv, meta_max_pages, 2, D], updated in place;
+ *              meta_max_pages * S >= per-sequence capacity, <= 16384
+ *   seqlens    (device) int32 [B], lengths after this step (L_b >= 1 appends;
+ *              L_b = 0 appends nothing)
+ *   k_new, v_new (device) fp16 [B, Hkv, D], both required
+ *   budget_tokens, page_idx, page_scores, workspace: as quest_page_score_topk
+ *   (the workspace size is da_quest_workspace_size(B, Hkv, meta_max_pages)).
+ */
+int quest_append_score_topk(const void* q, const da_kv_cache* kv, void* meta,
+                            int32_t meta_max_pages, const int32_t* seqlens, int32_t num_q_heads,
+                            int32_t budget_tokens, const void* k_new, const void* v_new,
+                            int32_t* page_idx, float* page_scores, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Attention over the chosen pages only.  [Quest-review] flowchart and worked
  * example (paper sections 3.3-3.5): exact attention over the real K/V of the
  * tokens in the chosen pages, [p*S, min(p*S + S, L_b)) for every p in

@@ -149,7 +149,8 @@ def test_full_quest_gqa_128k_step(da):
     """The long-context Quest GQA step: B=8, Hq=32, Hkv=8, D=128, L=131072,
     S=16, budget 4096 (K=256), 16 planted pages per unit.  Metadata is built
     in bulk, then the step appends one K/V row at slot 131071 with its
-    metadata update, scores and selects pages, and attends over them; dense
+    metadata update inside the score launch (quest_append_score_topk), scores
+    and selects pages, and attends over them; dense
     attention at the same shape (64 splits per unit) runs beside it.
     Sampled units are checked against the oracle run through the same steps."""
     b, hq, hkv, d, L, s, budget = 8, 32, 8, 128, 131072, 16, 4096
@@ -163,12 +164,11 @@ def test_full_quest_gqa_128k_step(da):
     torch.cuda.synchronize()
     k_before = {u: host(c["k"][u[0]:u[0] + 1, u[1]:u[1] + 1]) for u in units}
     v_before = {u: host(c["v"][u[0]:u[0] + 1, u[1]:u[1] + 1]) for u in units}
-    # the step
-    da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], 1, page_size=s, k_new=c["k_new"],
-                         v_new=c["v_new"])
+    # the step, as bench.py runs it: append fused into the score launch
     scores = torch.empty((b, hkv, P), dtype=torch.float32, device=DEV)
-    idx = da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s, budget_tokens=budget,
-                                   page_scores=scores)
+    idx = da.quest_append_score_topk(c["q"], c["k"], c["v"], meta, c["seqlens"], c["k_new"],
+                                     c["v_new"], page_size=s, budget_tokens=budget,
+                                     page_scores=scores)
     out = da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx,
                                       budget_tokens=budget, page_size=s)
     dense = da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"])

@@ -429,6 +429,70 @@ def test_quest_pipeline_end_to_end(da):
         assert max_err(host(out), want) <= ATOL
 
 
+# ------------------------------------------------------------ fused append + score
+
+
+@pytest.mark.parametrize("page_size,d,g,lens,paged", [
+    (16, 128, 4, [4096, 1000, 17, 33], False),   # mid-page, start of page (L-1 = 16, 32)
+    (8, 64, 2, [1024, 9, 0], False),              # page start (L-1 = 8), empty sequence
+    (16, 128, 4, [2000, 1601, 300], True),         # paged cache, L-1 = 1600 starts a page
+    (64, 64, 1, [640, 65], False),
+])
+def test_fused_append_score_matches_two_calls(da, page_size, d, g, lens, paged):
+    """quest_append_score_topk equals quest_meta_append (one step) followed by
+    quest_page_score_topk: cache, metadata, scores and chosen pages bitwise."""
+    hkv, cap = 2, max(lens) + 64
+    cap = (cap + page_size - 1) // page_size * page_size
+    if paged:
+        case = workloads.paged_case(900 + d, len(lens), hkv * g, hkv, d, page_size,
+                                    cap // page_size, lens, poison=False, spare_pages=3)
+        kw = dict(page_table=dev(case.page_table))
+    else:
+        case = workloads.dense_case(900 + d, len(lens), hkv * g, hkv, d, cap, lens)
+        kw = {}
+    rng = np.random.default_rng(901)
+    kn = rng.standard_normal((len(lens), hkv, d), dtype=np.float32).astype(np.float16)
+    vn = rng.standard_normal((len(lens), hkv, d), dtype=np.float32).astype(np.float16)
+    max_pages = cap // page_size
+    budget = 4 * page_size
+    sl = dev(case.seqlens)
+    outs = []
+    for fused in (False, True):
+        k, v = dev(case.k), dev(case.v)
+        meta = torch.zeros((len(lens), hkv, max_pages, 2, d), dtype=torch.float16, device=DEV)
+        # metadata of the lengths before the step (the new key not yet in it)
+        sl_before = dev(np.maximum(case.seqlens - 1, 0).astype(np.int32))
+        da.quest_meta_append(k, v, meta, sl_before, n_new=cap, page_size=page_size, **kw)
+        scores = torch.full((len(lens), hkv, max_pages), float("nan"), dtype=torch.float32,
+                            device=DEV)
+        if fused:
+            idx = da.quest_append_score_topk(dev(case.q), k, v, meta, sl, dev(kn), dev(vn),
+                                             page_size=page_size, budget_tokens=budget,
+                                             page_scores=scores, **kw)
+        else:
+            da.quest_meta_append(k, v, meta, sl, 1, page_size=page_size, k_new=dev(kn),
+                                 v_new=dev(vn), **kw)
+            idx = da.quest_page_score_topk(dev(case.q), meta, sl, page_size=page_size,
+                                           budget_tokens=budget, page_scores=scores)
+        torch.cuda.synchronize()
+        outs.append((host(k), host(v), host(meta), host(scores), host(idx)))
+    (k0, v0, m0, s0, i0), (k1, v1, m1, s1, i1) = outs
+    # slots past L hold NaN poison in both caches
+    assert np.array_equal(k0, k1, equal_nan=True) and np.array_equal(v0, v1, equal_nan=True)
+    assert np.array_equal(m0, m1, equal_nan=True)
+    for b, lb in enumerate(lens):
+        n = oquest.page_count(lb, page_size)
+        assert np.array_equal(s0[b, :, :n], s1[b, :, :n])
+    assert np.array_equal(i0, i1)
+    # and against the oracle: the metadata was built over [0, L - 1) before the
+    # step, so after it the pages hold the min/max of the final cache's keys
+    kc = oracle.gather_paged(k1, case.page_table, page_size, cap) if paged else k1
+    want = oquest.build_metadata(kc, case.seqlens, page_size, max_pages)
+    for b, lb in enumerate(lens):
+        n = oquest.page_count(lb, page_size)
+        assert np.array_equal(m1[b, :, :n], want[b, :, :n])
+
+
 # ------------------------------------------------------------ repeat_kv A/B
 
 
