@@ -20,18 +20,20 @@ batch of synthetic inputs already resident in HBM:
                dense at the same shape).
 
 Before every timed step a 1 GiB buffer is written (outside the step's events)
-so that neither L2 nor the 256 MiB Infinity Cache holds the inputs.  The step
-is captured once in a HIP graph; its time is the median over the K replays of
-HIP events around the replay on the launching stream.  `value` is the KV bytes
-the step must read divided by the step time.  A step is made of stages (the
-dense workloads: one stage of attention calls; Quest: KV + metadata append,
-page score + top-K, sparse attention).  The roofline entry is the dominant
-stage: its algorithmic bytes divided by its time, which for a one-stage step
-is the step time itself and otherwise the median over replays of the stage's
-own graph after a flush.  One attention call runs the attention kernel and
-the small split-merge kernel (or the score and top-K kernels), so both count.
-The CPU baseline is the fp64 NumPy oracle (1 BLAS thread) on a bounded sample
-of the same workload, timed on the host.
+so that neither L2 nor the 256 MiB Infinity Cache holds the inputs.  A step
+of at most three calls is launched directly on the stream (the host enqueues
+it while the flush kernel runs); a longer step is captured once in a HIP graph
+and replayed.  Step time is the median over the K steps of HIP events around
+the step on the launching stream.  `value` is the KV bytes the step must read
+divided by the step time.  A step is made of stages (the dense workloads: one
+stage of attention calls; Quest: page score + top-K with the fused append,
+sparse attention).  The roofline entry is the dominant stage: its algorithmic
+bytes divided by its time, which for a one-stage step is the step time itself
+and otherwise the median time of the stage's calls alone after a flush.  One
+attention call runs the attention kernel and the small split-merge kernel
+(or the score and top-K kernels), so both count.  The CPU baseline is the
+fp64 NumPy oracle (1 BLAS thread) on a bounded sample of the same workload,
+timed on the host.
 """
 
 import argparse
@@ -58,7 +60,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="exaone30",
                     choices=["exaone30", "gqa1", "paged", "quest32k", "quest128k",
-                             "repeat_kv_ab"])
+                             "repeat_kv_ab", "quest_sweep"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true",
@@ -250,6 +252,38 @@ def capture(torch, fns):
     return g
 
 
+DIRECT_MAX_CALLS = 3   # steps of at most this many calls are launched directly
+
+
+def time_direct(torch, fns, steps, warmup, flush):
+    """Launch the calls directly on the stream, warmup + steps times, with a
+    cache flush before each step (outside the events).  The host enqueues the
+    calls while the flush kernel (about 150 us) runs, so neither host launch
+    overhead nor a graph launch sits between the events.  Returns per-step ms."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    out = []
+    for i in range(warmup + steps):
+        if flush is not None:
+            flush.zero_()
+        a.record()
+        for f in fns:
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        if i >= warmup:
+            out.append(a.elapsed_time(b))
+    return out
+
+
+def time_calls(torch, fns, steps, warmup, flush):
+    """Per-step ms of the calls `fns`: launched directly when there are at most
+    DIRECT_MAX_CALLS of them, otherwise replayed from one captured graph."""
+    if len(fns) <= DIRECT_MAX_CALLS:
+        return time_direct(torch, fns, steps, warmup, flush), "direct"
+    return time_stages(torch, [capture(torch, fns)], steps, warmup, flush)[0], "graph"
+
+
 def time_stages(torch, graphs, steps, warmup, flush):
     """Replay the stage graphs back to back, warmup + steps times, with a cache
     flush before each step (outside the events) and HIP events between the
@@ -393,20 +427,26 @@ def counter_traffic(workload):
 
 
 def measure(torch, da, dev, step, steps, warmup, flush):
-    """Time the step as one captured graph (cache flush before every replay,
-    HIP events around it); with several stages, time each stage's own graph
-    the same way to find the dominant one.  A single-stage step is its own
-    dominant stage, timed in the same loop."""
+    """Time the step: a step of at most DIRECT_MAX_CALLS calls is launched
+    directly on the stream after the cache flush (HIP events around it);
+    longer steps are captured once in a HIP graph and replayed (a graph
+    launch costs about 12 us before its first kernel, which a long step
+    amortises and a short one would not).  With several stages, each stage is
+    timed the same way to find the dominant one; a single-stage step is its
+    own dominant stage, timed in the same loop."""
     for st in step.stages:       # eager warm-up allocates every workspace first
         for f in st.fns:
             f()
     if hasattr(step, "dense_fn"):
         step.dense_fn()
     torch.cuda.synchronize()
-    g_step = capture(torch, [f for st in step.stages for f in st.fns])
-    torch.cuda.synchronize()
+
+    def run(fns, reps, warm):
+        return time_calls(torch, fns, reps, warm, flush)
+
+    all_fns = [f for st in step.stages for f in st.fns]
     t_wall0 = time.perf_counter()
-    step_ms = time_stages(torch, [g_step], steps, warmup, flush)[0]
+    step_ms, how = run(all_fns, steps, warmup)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     ms = statistics.median(step_ms)
@@ -415,13 +455,15 @@ def measure(torch, da, dev, step, steps, warmup, flush):
     else:
         med = []
         for st in step.stages:
-            g = capture(torch, st.fns)
-            med.append(statistics.median(time_stages(torch, [g], max(10, steps // 2), 2,
-                                                     flush)[0]))
+            st_ms = run(st.fns, max(10, steps // 2), 2)[0]
+            med.append(statistics.median(st_ms))
+            if os.environ.get("BENCH_BOTH_LAUNCH_MODES"):
+                print(st.name, [round(x * 1e3, 2) for x in st_ms], file=sys.stderr)
     dom = max(range(len(med)), key=lambda j: med[j])
     dst = step.stages[dom]
     res = {
         "ms": ms,
+        "launch": how,
         "gbs": step.kv_bytes / (ms * 1e-3) / 1e9,
         "dominant": dst,
         "stage_ms": med[dom],
@@ -433,18 +475,20 @@ def measure(torch, da, dev, step, steps, warmup, flush):
         "stage_us": {st.name: round(m * 1e3, 3) for st, m in zip(step.stages, med)},
     }
     if hasattr(step, "separate_append_fns"):
-        g = capture(torch, step.separate_append_fns)
-        sep_ms = statistics.median(time_stages(torch, [g], steps, 2, flush)[0])
+        sep_ms = statistics.median(run(step.separate_append_fns, steps, 2)[0])
         res["step_us_separate_append"] = round(sep_ms * 1e3, 3)
     if hasattr(step, "dense_fn"):
-        g = capture(torch, [step.dense_fn])
-        dense_ms = statistics.median(time_stages(torch, [g], max(10, steps // 2), 2, flush)[0])
+        dense_ms = statistics.median(run([step.dense_fn], max(10, steps // 2), 2)[0])
         res["dense_same_shape_us"] = round(dense_ms * 1e3, 3)
         res["dense_same_shape_gbs"] = round(step.dense_bytes / (dense_ms * 1e-3) / 1e9, 1)
         res["dense_same_shape_pct_peak"] = round(
             100 * step.dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
         res["quest_over_dense_time"] = round(ms / dense_ms, 4)
         res["byte_model"] = step.byte_model
+    if os.environ.get("BENCH_BOTH_LAUNCH_MODES"):
+        g = capture(torch, all_fns)
+        res["us_per_step_graph"] = round(
+            statistics.median(time_stages(torch, [g], steps, warmup, flush)[0]) * 1e3, 3)
     return res
 
 
@@ -459,8 +503,7 @@ def repeat_kv_ab(da, torch, seed, dev, steps, warmup, flush):
     import numpy as np
 
     def timed(fns, reps):
-        g = capture(torch, fns)
-        return statistics.median(time_stages(torch, [g], reps, 2, flush)[0]) * 1e3
+        return statistics.median(time_calls(torch, fns, reps, 2, flush)[0]) * 1e3
 
     out = {}
     cases = []
@@ -519,6 +562,111 @@ def repeat_kv_ab(da, torch, seed, dev, steps, warmup, flush):
     return out
 
 
+def quest_sweep(da, torch, seed, dev, steps, warmup, flush):
+    """Quest page-size sweep at the Llama2-7B shape (B=1, H=32, D=128,
+    L=32768) for S in {8, 16, 32, 64}, at a fixed token budget (2048) and at
+    a fixed page count (K=128), against the byte model 1/S + B/L and dense
+    attention ([Quest-review], "is page size 16 always optimal"); and a
+    32-layer stack of that shape whose first two layers stay dense (the
+    paper's layer policy the review cites) against 32 dense layers."""
+    from decode_attention_folded_amd import workloads
+    import numpy as np
+    b, h, d, L = 1, 32, 128, 32768
+
+    def timed(fns, reps):
+        return statistics.median(time_calls(torch, fns, reps, 2, flush)[0]) * 1e3
+
+    c = workloads.device_dense(seed, b, h, h, d, L, L, dev, plant_pages=8, plant_page_size=16)
+    planted = c["planted"]
+    ws = da.Workspace(dev)
+    out = torch.empty_like(c["q"])
+    dense_us = timed([lambda: da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], out=out,
+                                                 workspace=ws)], steps)
+    dense_bytes = b * h * L * 2 * d * 2
+    sweep = {}
+    for S in (8, 16, 32, 64):
+        P = L // S
+        meta = torch.zeros((b, h, P, 2, d), dtype=torch.float16, device=dev)
+        da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], n_new=L, page_size=S)
+        for mode, budget in (("fixed_budget_2048", 2048), ("fixed_k_128", 128 * S)):
+            kp = budget // S
+            idx = torch.empty((b, h, kp), dtype=torch.int32, device=dev)
+            scores = torch.empty((b, h, P), dtype=torch.float32, device=dev)
+            fns = [lambda: da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=S,
+                                                    budget_tokens=budget, page_idx=idx,
+                                                    page_scores=scores),
+                   lambda: da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx,
+                                                       budget_tokens=budget, page_size=S,
+                                                       out=out, workspace=ws)]
+            for f in fns:
+                f()
+            torch.cuda.synchronize()
+            us = timed(fns, steps)
+            # planted 16-token blocks covered by the chosen pages (a statistic)
+            sel = idx.cpu().numpy()
+            hit = tot = 0
+            for (bb, hh), pages in planted.items():
+                chosen = set(int(p) for p in sel[bb, hh] if p >= 0)
+                for p16 in pages:
+                    toks = range(16 * p16, 16 * p16 + 16)
+                    hit += sum(1 for t in toks if t // S in chosen)
+                    tot += 16
+            model = 1.0 / S + budget / L
+            sweep[f"S{S}_{mode}"] = {
+                "page_size": S, "budget_tokens": budget, "k_pages": kp,
+                "step_us": round(us, 3), "over_dense_time": round(us / dense_us, 4),
+                "byte_model_ratio": round(model, 5),
+                "bytes": int(dense_bytes * model),
+                "gbs": round(dense_bytes * model / (us * 1e-6) / 1e9, 1),
+                "planted_token_recall": round(hit / tot, 4),
+            }
+        del meta
+        torch.cuda.empty_cache()
+    del c
+    torch.cuda.empty_cache()
+
+    # 32 layers of the same shape: all dense, or two dense + 30 Quest (S=16,
+    # budget 2048) layers
+    layers = []
+    for l in range(32):
+        cl = workloads.device_dense(seed * 1000 + l, b, h, h, d, L, L, dev)
+        cl["out"] = torch.empty_like(cl["q"])
+        if l >= 2:
+            cl["meta"] = torch.zeros((b, h, L // 16, 2, d), dtype=torch.float16, device=dev)
+            da.quest_meta_append(cl["k"], cl["v"], cl["meta"], cl["seqlens"], n_new=L,
+                                 page_size=16)
+            cl["idx"] = torch.empty((b, h, 128), dtype=torch.int32, device=dev)
+        layers.append(cl)
+
+    def dense_layer(cl):
+        da.gqa_decode_attn(cl["q"], cl["k"], cl["v"], cl["seqlens"], out=cl["out"], workspace=ws)
+
+    def quest_layer(cl):
+        da.quest_page_score_topk(cl["q"], cl["meta"], cl["seqlens"], page_size=16,
+                                 budget_tokens=2048, page_idx=cl["idx"])
+        da.quest_sparse_decode_attn(cl["q"], cl["k"], cl["v"], cl["seqlens"], cl["idx"],
+                                    budget_tokens=2048, page_size=16, out=cl["out"],
+                                    workspace=ws)
+
+    all_dense = [lambda cl=cl: dense_layer(cl) for cl in layers]
+    policy = [lambda cl=cl, l=l: dense_layer(cl) if l < 2 else quest_layer(cl)
+              for l, cl in enumerate(layers)]
+    for f in all_dense + policy:
+        f()
+    torch.cuda.synchronize()
+    reps = max(5, steps // 5)
+    t_dense = timed(all_dense, reps)
+    t_policy = timed(policy, reps)
+    stack = {"layers": 32, "dense_layers": 2, "page_size": 16, "budget_tokens": 2048,
+             "all_dense_us": round(t_dense, 3), "two_dense_then_quest_us": round(t_policy, 3),
+             "ratio": round(t_policy / t_dense, 4),
+             "byte_model_ratio": round((2 + 30 * (1 / 16 + 2048 / L)) / 32, 5)}
+    del layers
+    torch.cuda.empty_cache()
+    return {"dense_us": round(dense_us, 3), "dense_gbs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+            "sweep": sweep, "stack_32_layers": stack}
+
+
 MAKERS = {
     "exaone30": exaone30, "gqa1": gqa1, "paged": paged,
     "quest32k": lambda *a: quest(*a, long_ctx=False),
@@ -557,9 +705,25 @@ def main():
                          "stage": "repeat_kv copy, paged b64",
                          "bytes_per_call": big["copy_bytes"],
                          "us_per_call": big["repeat_kv_copy_us"],
-                         "time_source": "HIP events around replays of the call's graph after "
-                                        "a cache flush (median)"},
+                         "time_source": "HIP events around the call after a cache flush "
+                                        "(median)"},
             "repeat_kv_ab": ab,
+            "cache_flush_between_steps": flush is not None,
+        }
+        print(json.dumps(line), flush=True)
+        return 0
+    if args.workload == "quest_sweep":
+        sw = quest_sweep(da, torch, args.seed, dev, args.steps, args.warmup, flush)
+        base = sw["sweep"]["S16_fixed_budget_2048"]
+        line = {
+            "metric": "Quest score+topK+attn us/step (page-size sweep, 32K Llama2-7B shape)",
+            "value": base["step_us"], "unit": "us", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(base["step_us"] * 1e-3, 6),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16 in, f32 accumulate", "data": "synthetic N(0,1) fp16, seeded",
+            "config": {"workload": "quest_sweep_b1_h32_d128_L32768_S8-64",
+                       "value_is": "S=16, budget 2048"},
+            "quest_sweep": sw,
             "cache_flush_between_steps": flush is not None,
         }
         print(json.dumps(line), flush=True)
@@ -602,11 +766,10 @@ def main():
             "calls_per_step": len(r["dominant"].fns),
             "us_per_call": round(r["stage_ms"] * 1e3 / len(r["dominant"].fns), 3),
             "bytes_per_call": r["dominant"].bytes // len(r["dominant"].fns),
-            "time_source": ("HIP events around the step's graph replay in the timed "
-                            "region (median over steps), divided by its calls"
-                            if len(step.stages) == 1 else
-                            "HIP events around replays of the stage's own graph after a "
-                            "cache flush (median), divided by its calls"),
+            "time_source": ("HIP events around the step in the timed region (median over "
+                            "steps), divided by its calls" if len(step.stages) == 1 else
+                            "HIP events around the stage's calls alone after a cache "
+                            "flush (median), divided by its calls"),
         },
         "us_per_step": r["us_per_step"],
         "us_p10": r["us_p10"],
@@ -615,12 +778,14 @@ def main():
         "algorithmic_bytes_per_step": step.algo_bytes,
         "pct_hbm_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
         "cache_flush_between_steps": flush is not None,
-        "graph": "the step replayed from one captured HIP graph",
+        "launch": ("the step replayed from one captured HIP graph" if r["launch"] == "graph"
+                   else "the step's calls launched directly on the stream"),
         "timed_wall_s": r["timed_wall_s"],
         "stage_us": r["stage_us"],
     }
     for key in ("dense_same_shape_us", "dense_same_shape_gbs", "dense_same_shape_pct_peak",
-                "quest_over_dense_time", "byte_model", "step_us_separate_append"):
+                "quest_over_dense_time", "byte_model", "step_us_separate_append",
+                "us_per_step_graph"):
         if key in r:
             line[key] = r[key]
 
