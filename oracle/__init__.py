@@ -17,8 +17,9 @@ Sources (cited by page title and section only):
 
 Modules:
 
-* ``oracle.dense``  -- repeat_kv decode attention (the plain definition), the
-  paged-address gather, the KV append.
+* ``oracle.dense``  -- repeat_kv decode attention (the plain definition), its
+  q_len > 1 form with the causal alignment, the paged-address gather, the KV
+  append.
 * ``oracle.quest``  -- page min/max metadata, the page score U(p, q), top-K
   selection and attention restricted to the selected pages.
 * ``oracle.bytes_model`` -- algorithmic byte counts and the Quest read-bytes
@@ -37,6 +38,7 @@ from .dense import (  # noqa: F401
     append_kv,
     gather_paged,
     decode_attention,
+    multi_query_attention,
 )
 from .quest import (  # noqa: F401
     page_count,

@@ -113,3 +113,43 @@ def decode_attention(q, k_cache, v_cache, seqlens, scale, token_mask=None):
             prob = e / np.sum(e)
             out[b, h] = prob @ v_rep[h]
     return out
+
+
+def multi_query_attention(q, k_cache, v_cache, seqlens, scale):
+    """Attention for q_len > 1 new tokens per sequence over a GQA cache, float64.
+
+    [CoreML-GQA] section 5 "Limitations and Next Steps" ("Prefill Needs
+    Separate Design"): with more than one query position per head, the grouped
+    path must also align the causal mask.  Reading used here (chunked prefill,
+    speculative verify): the q_len queries of sequence b sit at its last q_len
+    positions L_b - q_len .. L_b - 1 (their keys are already in the cache), and
+    query i attends to the keys t <= L_b - q_len + i.  Written the plain way:
+    repeat_kv, then per head and per query a softmax over that key prefix.
+
+    * ``q``: [B, Hq, Lq, D]; ``k_cache``/``v_cache``: [B, Hkv, cap, D];
+      ``seqlens[b]`` = L_b (clamped to [0, cap]).
+    * A query with no key (L_b - q_len + i < 0) returns zeros.
+
+    Returns float64 [B, Hq, Lq, D].
+    """
+    q64 = np.asarray(q, dtype=np.float64)
+    bsz, hq, lq, d = q64.shape
+    hkv = k_cache.shape[1]
+    assert hq % hkv == 0
+    n_rep = hq // hkv
+    out = np.zeros((bsz, hq, lq, d), dtype=np.float64)
+    for b in range(bsz):
+        lb = max(0, min(int(seqlens[b]), k_cache.shape[2]))
+        if lb == 0:
+            continue
+        k_rep = repeat_kv(np.asarray(k_cache[b:b + 1, :, :lb, :], dtype=np.float64), n_rep)[0]
+        v_rep = repeat_kv(np.asarray(v_cache[b:b + 1, :, :lb, :], dtype=np.float64), n_rep)[0]
+        for i in range(lq):
+            visible = lb - lq + 1 + i          # keys 0 .. L_b - q_len + i
+            if visible <= 0:
+                continue
+            for h in range(hq):
+                scores = (k_rep[h, :visible] @ q64[b, h, i]) * scale
+                e = np.exp(scores - np.max(scores))
+                out[b, h, i] = (e / np.sum(e)) @ v_rep[h, :visible]
+    return out

@@ -82,6 +82,69 @@ def test_matches_torch_sdpa_fp64(group, seqlens):
     np.testing.assert_allclose(ref, lib, rtol=0, atol=1e-12)
 
 
+# ----------------------------------------------------------- q_len > 1
+
+
+def _causal_mask(seqlens, lq, cap):
+    """Boolean [B, 1, Lq, cap]: query i of sequence b (position L_b - Lq + i)
+    sees key t iff t <= L_b - Lq + i."""
+    pos = torch.tensor(seqlens)[:, None, None, None] - lq + torch.arange(lq)[None, None, :, None]
+    return torch.arange(cap)[None, None, None, :] <= pos
+
+
+@pytest.mark.parametrize("group,lq,seqlens", [(4, 2, [33, 2, 17]), (1, 8, [8, 9, 40]),
+                                              (2, 4, [64, 5, 4])])
+def test_multi_query_matches_torch_sdpa_fp64(group, lq, seqlens):
+    """Library special case for the q_len > 1 reading: torch's
+    scaled_dot_product_attention in float64 on the CPU, native GQA broadcast,
+    with an explicit position mask (query i of a sequence of length L sits at
+    L - q_len + i and sees keys up to its own position)."""
+    hkv, d, cap = 2, 32, 64
+    case = workloads.dense_case(13, 3, hkv * group, hkv, d, cap, seqlens, poison=False)
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((3, hkv * group, lq, d), dtype=np.float32).astype(np.float16)
+    ref = oracle.multi_query_attention(q, case.k, case.v, case.seqlens, case.scale)
+    lib = F.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64)), torch.from_numpy(case.k.astype(np.float64)),
+        torch.from_numpy(case.v.astype(np.float64)), attn_mask=_causal_mask(seqlens, lq, cap),
+        scale=case.scale, enable_gqa=True).numpy()
+    np.testing.assert_allclose(ref, lib, rtol=0, atol=1e-12)
+
+
+def test_multi_query_special_cases():
+    """q_len = 1 is single-token decode; with L = q_len the first query sees
+    only key 0 (o = v_0 exactly) and the last sees every key; a query before
+    the start of the sequence (L < q_len) gets zeros."""
+    hkv, g, d, cap = 2, 4, 64, 32
+    case = workloads.dense_case(15, 2, hkv * g, hkv, d, cap, [20, 5])
+    q1 = case.q[:, :, None, :]
+    np.testing.assert_array_equal(
+        oracle.multi_query_attention(q1, case.k, case.v, case.seqlens, case.scale)[:, :, 0],
+        oracle.decode_attention(case.q, case.k, case.v, case.seqlens, case.scale))
+    rng = np.random.default_rng(16)
+    lq = 5
+    q = rng.standard_normal((2, hkv * g, lq, d), dtype=np.float32).astype(np.float16)
+    out = oracle.multi_query_attention(q, case.k, case.v, [20, 5], case.scale)
+    for h in range(hkv * g):
+        np.testing.assert_array_equal(out[1, h, 0], case.v[1, h // g, 0].astype(np.float64))
+    last = oracle.decode_attention(q[:, :, lq - 1], case.k, case.v, [20, 5], case.scale)
+    np.testing.assert_allclose(out[:, :, lq - 1], last, rtol=0, atol=1e-12)
+    short = oracle.multi_query_attention(q, case.k, case.v, [3, 5], case.scale)
+    assert np.all(short[0, :, :2] == 0.0) and np.all(short[0, :, 2:] != 0.0)
+
+
+def test_mutation_multi_query_off_by_one_is_caught(monkeypatch):
+    real = odense.multi_query_attention
+
+    def one_key_short(q, k, v, seqlens, scale):
+        # each query sees one key fewer than its own position
+        out = real(q, k, v, [int(l) - 1 for l in seqlens], scale)
+        return out
+    monkeypatch.setattr(oracle, "multi_query_attention", one_key_short)
+    with pytest.raises(AssertionError):
+        test_multi_query_matches_torch_sdpa_fp64(4, 2, [33, 2, 17])
+
+
 def test_single_key_returns_its_value():
     """With one valid key the softmax is exactly 1: o = v_0 for every query
     head of the group."""
