@@ -60,7 +60,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="exaone30",
                     choices=["exaone30", "gqa1", "paged", "quest32k", "quest128k",
-                             "repeat_kv_ab", "quest_sweep"])
+                             "repeat_kv_ab", "quest_sweep", "multi_query"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true",
@@ -562,6 +562,43 @@ def repeat_kv_ab(da, torch, seed, dev, steps, warmup, flush):
     return out
 
 
+def multi_query(da, torch, seed, dev, steps, warmup, flush):
+    """The fold with q_len > 1 query positions per head (group and sequence
+    axes merged, causal alignment per row): the K/V bytes of a step stay the
+    same while the rows per KV head grow from G to G * q_len."""
+    from decode_attention_folded_amd import workloads
+
+    def timed(fns, reps):
+        return statistics.median(time_calls(torch, fns, reps, 2, flush)[0]) * 1e3
+
+    out = {}
+    shapes = (("exaone_30_layers_len3000", 30, 1, 32, 8, 64, 4096, 3000, (1, 2)),
+              ("dense_b1_h32_g1_d128_L32768", 1, 1, 32, 32, 128, 32768, 32768, (1, 2, 4, 8)),
+              ("dense_b8_hq32_hkv8_d128_L131072", 1, 8, 32, 8, 128, 131072, 131072, (1, 2)))
+    for name, layers, b, hq, hkv, d, cap, L, qlens in shapes:
+        data = [workloads.device_dense(seed * 100 + l, b, hq, hkv, d, cap, L, dev)
+                for l in range(layers)]
+        ws = da.Workspace(dev)
+        kv_bytes = layers * b * hkv * L * 2 * d * 2
+        res = {}
+        for lq in qlens:
+            qs = [torch.randn((b, hq, lq, d), device=dev).to(torch.float16) for _ in data]
+            outs = [torch.empty_like(q) for q in qs]
+            fns = [lambda c=c, q=q, o=o: da.gqa_decode_attn_multi(q, c["k"], c["v"], c["seqlens"],
+                                                                  out=o, workspace=ws)
+                   for c, q, o in zip(data, qs, outs)]
+            for f in fns:
+                f()
+            torch.cuda.synchronize()
+            us = timed(fns, steps if L < 100000 else max(10, steps // 2))
+            res[f"q_len_{lq}"] = {"rows_per_kv_head": hq // hkv * lq, "step_us": round(us, 3),
+                                  "kv_gbs": round(kv_bytes / (us * 1e-6) / 1e9, 1)}
+        out[name] = res
+        del data
+        torch.cuda.empty_cache()
+    return out
+
+
 def quest_sweep(da, torch, seed, dev, steps, warmup, flush):
     """Quest page-size sweep at the Llama2-7B shape (B=1, H=32, D=128,
     L=32768) for S in {8, 16, 32, 64}, at a fixed token budget (2048) and at
@@ -708,6 +745,23 @@ def main():
                          "time_source": "HIP events around the call after a cache flush "
                                         "(median)"},
             "repeat_kv_ab": ab,
+            "cache_flush_between_steps": flush is not None,
+        }
+        print(json.dumps(line), flush=True)
+        return 0
+    if args.workload == "multi_query":
+        mq = multi_query(da, torch, args.seed, dev, args.steps, args.warmup, flush)
+        ex = mq["exaone_30_layers_len3000"]
+        line = {
+            "metric": "decode-attn KV GB/s with q_len > 1 queries per head (fold, causal)",
+            "value": ex["q_len_2"]["kv_gbs"], "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ex["q_len_2"]["step_us"] * 1e-3, 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16 in, f32 accumulate",
+            "data": "synthetic N(0,1) fp16, seeded",
+            "config": {"workload": "multi_query: exaone 30 layers, dense 32K G=1, dense 128K G=4",
+                       "value_is": "exaone 30 layers at q_len 2"},
+            "multi_query": mq,
             "cache_flush_between_steps": flush is not None,
         }
         print(json.dumps(line), flush=True)

@@ -28,7 +28,7 @@ STATUS_NAMES = {
 EXPORTED_SYMBOLS = (
     "da_status_string", "da_workspace_size", "gqa_decode_attn", "quest_meta_append",
     "da_quest_workspace_size", "quest_page_score_topk", "quest_sparse_decode_attn",
-    "gqa_repeat_kv", "quest_append_score_topk",
+    "gqa_repeat_kv", "quest_append_score_topk", "gqa_decode_attn_multi",
 )
 
 
@@ -86,6 +86,10 @@ def load_library():
         lib.quest_page_score_topk.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, P, P,
                                               P, SZ, P]
         lib.quest_sparse_decode_attn.argtypes = [P, KVP, P, P, I32, I32, F32, P, P, SZ, I32, P]
+        lib.gqa_decode_attn_multi.argtypes = [P, KVP, P, I32, I32, F32, P, P, SZ, I32, P]
+        lib.gqa_repeat_kv.argtypes = [KVP, I32, P, P, P, P]
+        lib.quest_append_score_topk.argtypes = [P, KVP, P, I32, P, I32, I32, P, P, P, P, P, SZ,
+                                                P]
         for name in EXPORTED_SYMBOLS[1:]:
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
@@ -245,6 +249,40 @@ def gqa_decode_attn(q, k_cache, v_cache, seqlens, *, scale=None, k_new=None, v_n
                                _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(ws), ws.numel(),
                                num_splits, _stream_handle(q.device, stream)),
            "gqa_decode_attn")
+    return out
+
+
+def gqa_decode_attn_multi(q, k_cache, v_cache, seqlens, *, scale=None, page_table=None,
+                          page_size=0, out=None, workspace=None, num_splits=0, stream=None):
+    """Folded GQA attention for q_len > 1 queries per head (see
+    ``gqa_decode_attn_multi`` in decode_attn.h): q [B, Hq, q_len, D] fp16, the
+    last q_len positions of each sequence, causally aligned.  Returns out
+    [B, Hq, q_len, D] fp16."""
+    lib = load_library()
+    _need(q, "q", torch.float16, 4)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    batch, hq, q_len, d = q.shape
+    desc = _kv_desc(k_cache, v_cache, batch, page_table, page_size)
+    if seqlens.shape[0] != batch:
+        raise ValueError("seqlens must be [B]")
+    if desc.head_dim != d:
+        raise ValueError("q and the cache disagree on head_dim")
+    if hq % desc.num_kv_heads != 0:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float16, 4)
+    if out.shape != q.shape:
+        raise ValueError("out must be [B, Hq, q_len, D]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = ctypes.c_size_t()
+    _check(lib.da_workspace_size(ctypes.byref(desc), hq * q_len, 0, num_splits,
+                                 ctypes.byref(nbytes)), "da_workspace_size")
+    ws = _workspace(workspace, q.device).get(nbytes.value, q.device)
+    _check(lib.gqa_decode_attn_multi(_ptr(q), ctypes.byref(desc), _ptr(seqlens), hq, q_len,
+                                     scale, _ptr(out), _ptr(ws), ws.numel(), num_splits,
+                                     _stream_handle(q.device, stream)),
+           "gqa_decode_attn_multi")
     return out
 
 

@@ -134,12 +134,14 @@ int check_budget(const Shape& s, int budget_tokens) {
   return DA_OK;
 }
 
+// num_rows = Hq * q_len: the kernel reads Q [B, Hq, q_len, D] as
+// [B, Hkv, G * q_len, D] rows.
 int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
-                  const int32_t* page_idx, int32_t budget_tokens, int32_t num_q_heads,
-                  float scale, const void* k_new, const void* v_new, void* out, void* workspace,
-                  size_t workspace_bytes, int32_t num_splits, void* stream) {
+                  const int32_t* page_idx, int32_t budget_tokens, int32_t num_rows,
+                  int32_t q_len, float scale, const void* k_new, const void* v_new, void* out,
+                  void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
   Shape s;
-  int st = check_cache(kv, num_q_heads, &s);
+  int st = check_cache(kv, num_rows, &s);
   if (st != DA_OK) return st;
   if ((k_new == nullptr) != (v_new == nullptr)) return DA_ERR_NULL;
   if (!isfinite(scale)) return DA_ERR_SHAPE;
@@ -180,6 +182,7 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
   a.batch = s.batch;
   a.num_kv_heads = s.hkv;
   a.group = s.group;
+  a.q_len = q_len;
   a.head_dim = s.d;
   a.capacity = s.capacity;
   a.cache_stride = s.stride;
@@ -233,8 +236,20 @@ int gqa_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens
                     int32_t num_q_heads, float scale, const void* k_new, const void* v_new,
                     void* out, void* workspace, size_t workspace_bytes, int32_t num_splits,
                     void* stream) {
-  return run_attention(q, kv, seqlens, nullptr, 0, num_q_heads, scale, k_new, v_new, out,
+  return run_attention(q, kv, seqlens, nullptr, 0, num_q_heads, 1, scale, k_new, v_new, out,
                        workspace, workspace_bytes, num_splits, stream);
+}
+
+int gqa_decode_attn_multi(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
+                          int32_t num_q_heads, int32_t q_len, float scale, void* out,
+                          void* workspace, size_t workspace_bytes, int32_t num_splits,
+                          void* stream) {
+  if (kv == nullptr) return DA_ERR_NULL;
+  if (q_len < 1 || num_q_heads < 1 || kv->num_kv_heads < 1) return DA_ERR_SHAPE;
+  if (num_q_heads % kv->num_kv_heads != 0) return DA_ERR_SHAPE;
+  if ((int64_t)num_q_heads * q_len > INT32_MAX / 2) return DA_ERR_SHAPE;
+  return run_attention(q, kv, seqlens, nullptr, 0, num_q_heads * q_len, q_len, scale, nullptr,
+                       nullptr, out, workspace, workspace_bytes, num_splits, stream);
 }
 
 int quest_sparse_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
@@ -242,7 +257,7 @@ int quest_sparse_decode_attn(const void* q, const da_kv_cache* kv, const int32_t
                              int32_t num_q_heads, float scale, void* out, void* workspace,
                              size_t workspace_bytes, int32_t num_splits, void* stream) {
   if (page_idx == nullptr) return DA_ERR_NULL;
-  return run_attention(q, kv, seqlens, page_idx, budget_tokens, num_q_heads, scale, nullptr,
+  return run_attention(q, kv, seqlens, page_idx, budget_tokens, num_q_heads, 1, scale, nullptr,
                        nullptr, out, workspace, workspace_bytes, num_splits, stream);
 }
 

@@ -111,6 +111,7 @@ struct Stage {
   f16x8 v0[Layout<D>::NCV];  // key (lane % 8)
   f16x8 v1[Layout<D>::NCV];  // key (lane % 8) + 8
   bool kvalid;               // the K key of this lane
+  int ktok;                  // its token position (causal limit of q_len > 1 rows)
 };
 
 // Merge the split partials of one unit into its G output rows:
@@ -120,11 +121,11 @@ struct Stage {
 // the first batch is read before `get_nsplit` is called (it may wait for the
 // valid length).  Splits past the valid ones are dropped by selects, so stale
 // workspace contents never enter the sums.
-template <int D, int G, typename NSplitFn>
+template <int D, int G, int NT, typename NSplitFn>
 __device__ __forceinline__ void merge_partials(const AttnLaunch& a, int64_t unit,
                                                NSplitFn get_nsplit) {
-  constexpr int kIters = (G * D + kThreads - 1) / kThreads;  // 1, 2 or 4
-  constexpr int kBatch = 32 / kIters;                          // splits per load batch
+  constexpr int kIters = (G * D + NT - 1) / NT;  // output elements per thread
+  constexpr int kBatch = 32 / kIters;            // splits per load batch
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + unit * a.max_splits * G;
   const float* po = a.part_o + unit * a.max_splits * G * D;
   f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;
@@ -142,7 +143,7 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, int64_t unit
     float ov[kIters][kBatch];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
-      const int i = min((int)threadIdx.x + it * kThreads, G * D - 1);
+      const int i = min((int)threadIdx.x + it * NT, G * D - 1);
       const int g = i / D;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -176,7 +177,7 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, int64_t unit
   }
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
-    const int i = (int)threadIdx.x + it * kThreads;
+    const int i = (int)threadIdx.x + it * NT;
     if (i < G * D) out[i] = (f16)(S[it] > 0.0f ? O[it] / S[it] : 0.0f);
   }
 }
@@ -323,6 +324,13 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   const f16* knew_row = has_new ? reinterpret_cast<const f16*>(a.k_new) + unit * D : nullptr;
   const f16* vnew_row = has_new ? reinterpret_cast<const f16*>(a.v_new) + unit * D : nullptr;
 
+  // Row r of the unit is query position r % q_len of head G * kv + r / q_len
+  // (group and sequence axes merged); it sees keys t < L - q_len + 1 + r % q_len.
+  // With q_len = 1 every row sees the whole valid length.
+  int lim[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) lim[g] = L - a.q_len + 1 + g % a.q_len;
+
   float m[G], l[G], acc[G][NV];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -394,6 +402,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
     const int64_t o0 = resolve(j0 + rv, live, v0, t0);
     const int64_t o1 = resolve(j0 + rv + 8, live, v1, t1);
     st.kvalid = vk;
+    st.ktok = tk;
     // The appended key reads k_new/v_new; with an append, masked keys read it
     // too (the slot being written may not hold finite data yet).
     const f16* kp = (has_new && (!vk || tk == L - 1)) ? knew_row : kc + ok;
@@ -446,7 +455,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
     float sa[G], sb[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float mine = st.kvalid ? sk[g] * a.scale_log2 : -INFINITY;
+      const float mine = (st.kvalid && st.ktok < lim[g]) ? sk[g] * a.scale_log2 : -INFINITY;
       const float other = lane_xor<8>(mine);
       sa[g] = upper ? other : mine;
       sb[g] = upper ? mine : other;
@@ -555,13 +564,15 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   }
 }
 
-// Merge kernel: one workgroup per (b, kv) unit.
+// Merge kernel: one workgroup per (b, kv) unit, one thread per output element
+// of the unit's G rows (G * D threads, 64 to 1024), so every thread merges a
+// batch of up to 32 splits with one round of loads.
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads) merge_kernel(AttnLaunch a, bool sparse) {
+__global__ void __launch_bounds__(G * D) merge_kernel(AttnLaunch a, bool sparse) {
   const int kv = blockIdx.x;
   const int b = blockIdx.y;
   const int64_t unit = (int64_t)b * a.num_kv_heads + kv;
-  merge_partials<D, G>(a, unit, [&] { return stream_info(a, b, sparse).nsplit; });
+  merge_partials<D, G, G * D>(a, unit, [&] { return stream_info(a, b, sparse).nsplit; });
 }
 
 template <int D, int G, bool PAGED, bool SPARSE>
@@ -576,7 +587,7 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
   }
   const int err = (int)hipGetLastError();
   if (err != 0 || a.max_splits <= 1) return err;
-  hipLaunchKernelGGL((merge_kernel<D, G>), dim3(a.num_kv_heads, a.batch), dim3(kThreads), 0,
+  hipLaunchKernelGGL((merge_kernel<D, G>), dim3(a.num_kv_heads, a.batch), dim3(G * D), 0,
                      stream, a, SPARSE);
   return (int)hipGetLastError();
 }

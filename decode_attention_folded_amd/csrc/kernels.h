@@ -24,7 +24,8 @@ struct AttnLaunch {
   float* part_o;             // [B * Hkv, max_splits, G, D]
   int32_t batch;
   int32_t num_kv_heads;
-  int32_t group;             // G = Hq / Hkv
+  int32_t group;             // rows per KV head: (Hq / Hkv) * q_len
+  int32_t q_len;             // query positions per head (the last q_len of each sequence)
   int32_t head_dim;          // D
   int32_t capacity;          // valid-length clamp: cap (contiguous) or max_pages * S
   int32_t cache_stride;      // slots per (b, kv) row of a contiguous cache

@@ -121,6 +121,29 @@ int gqa_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens
                     void* stream);
 
 /*
+ * Folded GQA attention for q_len > 1 query positions per head (chunked
+ * prefill, speculative verify).  [CoreML-GQA] section 5 "Limitations and Next
+ * Steps" ("Prefill Needs Separate Design"): the group and sequence axes are
+ * merged into one row axis, and the causal mask is aligned per row.  Q
+ * [B, Hq, q_len, D] is read as [B, Hkv, G * q_len, D]; every K/V row is read
+ * once for all G * q_len rows.  The q_len queries are the last q_len positions
+ * of each sequence: query i of sequence b attends to keys
+ * t <= L_b - q_len + i (their own K/V rows must already be in the cache);
+ * a query with no such key (L_b - q_len + i < 0) yields zeros.
+ *
+ *   q          (device) fp16 [B, Hq, q_len, D]
+ *   q_len      1 <= q_len; G * q_len must be in {1, 2, 4, 8}
+ *   out        (device) fp16 [B, Hq, q_len, D]
+ *   workspace  >= da_workspace_size(kv, Hq * q_len, 0, num_splits) bytes
+ *   other arguments as gqa_decode_attn (no append: write the new rows first).
+ * With q_len = 1 the result equals gqa_decode_attn without an append.
+ */
+int gqa_decode_attn_multi(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
+                          int32_t num_q_heads, int32_t q_len, float scale, void* out,
+                          void* workspace, size_t workspace_bytes, int32_t num_splits,
+                          void* stream);
+
+/*
  * Materialised repeat_kv, the copy the fold removes; for A/B comparison only.
  * [CoreML-GQA] section 2 "Why Does GQA Replicate KV?" (and "expand Is a View,
  * but reshape Introduces a Copy"): the GQA reference path copies each KV head

@@ -43,6 +43,30 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_every_entry_point_has_declared_argument_types(lib):
+    """ctypes must know every argument type (size_t and float arguments are
+    passed wrongly without them)."""
+    from decode_attention_folded_amd import _binding
+    for n in _binding.EXPORTED_SYMBOLS:
+        assert getattr(lib, n).argtypes is not None, n
+
+
+def test_multi_query_validation_codes(lib):
+    P = ctypes.c_void_p
+    d = _desc()
+
+    def call(hq=32, q_len=2, desc=d, q=FAKE, out=FAKE, ws_bytes=1 << 30):
+        return lib.gqa_decode_attn_multi(P(q), ctypes.byref(desc), P(FAKE), hq, q_len, 0.125,
+                                         P(out), P(FAKE), ws_bytes, 0, None)
+    assert call(q_len=0) == -2
+    assert call(hq=30) == -2
+    assert call(q_len=3) == -3          # G * q_len = 12
+    assert call(hq=64, q_len=2) == -3   # G * q_len = 16
+    assert call(q=0) == -1
+    assert call(ws_bytes=16) == -5
+    assert call(desc=_desc(batch=0), q=0, out=0) == 0
+
+
 def test_status_strings(lib):
     for code in range(0, -7, -1):
         s = lib.da_status_string(code).decode()

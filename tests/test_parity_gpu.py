@@ -429,6 +429,55 @@ def test_quest_pipeline_end_to_end(da):
         assert max_err(host(out), want) <= ATOL
 
 
+# ------------------------------------------------------------ q_len > 1
+
+
+@pytest.mark.parametrize("d,g,lq,cap,lens,splits", [
+    (64, 4, 2, 700, [700, 130, 2, 1], 0),
+    (128, 2, 4, 600, [600, 4, 3, 257], 0),
+    (128, 1, 8, 500, [500, 8, 5, 33], 0),
+    (64, 1, 2, 300, [300, 17], 7),
+    (128, 4, 2, 1100, [1100, 999], 1),
+    (64, 8, 1, 400, [400, 2], 0),
+])
+def test_multi_query_parity(da, d, g, lq, cap, lens, splits):
+    """G * q_len rows per KV head, causal alignment per row, against the
+    oracle; includes sequences shorter than q_len (leading rows see no key)
+    and split counts from 1 to several."""
+    hkv = 2
+    case = workloads.dense_case(950 + g * lq, len(lens), hkv * g, hkv, d, cap, lens)
+    rng = np.random.default_rng(951)
+    q = rng.standard_normal((len(lens), hkv * g, lq, d), dtype=np.float32).astype(np.float16)
+    out = da.gqa_decode_attn_multi(dev(q), dev(case.k), dev(case.v), dev(case.seqlens),
+                                   num_splits=splits)
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    want = oracle.multi_query_attention(q, case.k, case.v, case.seqlens, case.scale)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, want) <= ATOL
+
+
+def test_multi_query_paged_and_q1_equals_decode(da):
+    """Paged cache with q_len = 4; and q_len = 1 gives the decode result
+    bitwise."""
+    case = workloads.paged_case(960, 3, 8, 2, 128, 16, 40, [640, 4, 300])
+    rng = np.random.default_rng(961)
+    q = rng.standard_normal((3, 8, 2, 128), dtype=np.float32).astype(np.float16)
+    out = da.gqa_decode_attn_multi(dev(q), dev(case.k), dev(case.v), dev(case.seqlens),
+                                   page_table=dev(case.page_table), page_size=16)
+    torch.cuda.synchronize()
+    kc = oracle.gather_paged(case.k, case.page_table, 16, 40 * 16)
+    vc = oracle.gather_paged(case.v, case.page_table, 16, 40 * 16)
+    want = oracle.multi_query_attention(q, kc, vc, case.seqlens, case.scale)
+    assert max_err(host(out), want) <= ATOL
+    dc = workloads.dense_case(962, 2, 32, 8, 64, 900, [900, 77])
+    one = da.gqa_decode_attn_multi(dev(dc.q[:, :, None, :]), dev(dc.k), dev(dc.v),
+                                   dev(dc.seqlens))
+    dec = da.gqa_decode_attn(dev(dc.q), dev(dc.k), dev(dc.v), dev(dc.seqlens))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(one)[:, :, 0], host(dec))
+
+
 # ------------------------------------------------------------ fused append + score
 
 
