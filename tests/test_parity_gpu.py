@@ -316,6 +316,35 @@ def test_score_topk_parity(da, page_size, budget, g, d, cap, lens):
     assert np.array_equal(host(idx2), host(idx))
 
 
+@pytest.mark.parametrize("n_pages,k_pages,seqlen_pages", [
+    (4096, 300, 4096),      # 16 items per thread
+    (3001, 64, 2999),       # 16 items per thread, ragged
+    (16384, 1000, 16384),   # the maximum: 64 items per thread
+    (12000, 5, 11111),      # 64 items per thread, ragged, small K
+])
+def test_topk_large_page_counts(da, n_pages, k_pages, seqlen_pages):
+    """Score + top-K on random metadata up to the supported maximum of
+    16384 pages per (b, kv): every item-per-thread width of the select."""
+    s, d, g, hkv = 8, 64, 2, 2
+    rng = np.random.default_rng(n_pages)
+    a = rng.standard_normal((1, hkv, n_pages, d), dtype=np.float32)
+    b = rng.standard_normal((1, hkv, n_pages, d), dtype=np.float32)
+    meta = np.stack([np.minimum(a, b), np.maximum(a, b)], axis=3).astype(np.float16)
+    q = rng.standard_normal((1, hkv * g, d), dtype=np.float32).astype(np.float16)
+    seqlens = np.array([seqlen_pages * s - 3], np.int32)
+    scores = torch.empty((1, hkv, n_pages), dtype=torch.float32, device=DEV)
+    idx = da.quest_page_score_topk(dev(q), dev(meta), dev(seqlens), page_size=s,
+                                   budget_tokens=k_pages * s, page_scores=scores)
+    torch.cuda.synchronize()
+    want_scores = oquest.page_scores(q, meta, seqlens, s)
+    want_idx = oquest.select_pages(want_scores, seqlens, s, k_pages)
+    got_scores = host(scores).astype(np.float64)
+    n = oquest.page_count(seqlens[0], s)
+    tol = score_tolerance(q, meta, seqlens, s)
+    assert np.all(np.abs(got_scores[0, :, :n] - want_scores[0, :, :n]) <= tol[0, :, :n])
+    check_selection(host(idx), got_scores, want_idx, want_scores, seqlens, s, k_pages)
+
+
 def test_topk_exact_ties_lower_index(da):
     """Pages with identical keys tie exactly in fp32 too; the lower index is
     chosen.  Many ties straddle the K-th position here."""
