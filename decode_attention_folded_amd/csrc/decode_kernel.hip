@@ -5,8 +5,12 @@
 // h = G*kv + g are treated as G rows of one small matrix, so each K and V row
 // is read from HBM once for all G rows (no repeat_kv copy).  Per row:
 // s_t = scale * q.k_t for t < L_b, softmax over t, o = sum_t p_t v_t.
-// The Quest variant ([Quest-review], paper sections 3.3-3.5) runs the same
-// loop over the tokens of the chosen pages only.
+// With q_len > 1 query positions per head ([CoreML-GQA] section 5, "Prefill
+// Needs Separate Design") the rows are the G * q_len (head, position) pairs of
+// the KV head -- group and sequence axes merged -- and row g * q_len + i only
+// sees keys t < L_b - q_len + 1 + i.  The template parameter G is the row
+// count.  The Quest variant ([Quest-review], paper sections 3.3-3.5) runs the
+// same loop over the tokens of the chosen pages only.
 //
 // Work decomposition (flash-decode): a 1-D grid of splits x (B * Hkv) units,
 // unit index fastest.  A workgroup of 4 waves owns a contiguous chunk of
