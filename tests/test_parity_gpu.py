@@ -614,6 +614,61 @@ def test_repeat_kv_from_paged_cache(da):
         assert np.array_equal(host(vr)[b, :, :lb], want_v[b, :, :lb])
 
 
+def test_graph_replays_match_eager(da):
+    """The calls captured in a HIP graph (dense decode with append, the fused
+    Quest step, sparse attention) give the eager results on every replay,
+    with unrelated eager work and synchronisations between the replays."""
+    case = workloads.dense_case(980, 2, 32, 8, 128, 2048, [2048, 1500], with_new=True)
+    s, budget = 16, 256
+    q, sl = dev(case.q), dev(case.seqlens)
+    kn, vn = dev(case.k_new), dev(case.v_new)
+
+    def fresh():
+        k, v = dev(case.k), dev(case.v)
+        meta = torch.zeros((2, 8, 2048 // s, 2, 128), dtype=torch.float16, device=DEV)
+        sl_before = dev(case.seqlens - 1)
+        da.quest_meta_append(k, v, meta, sl_before, n_new=2048, page_size=s)
+        return k, v, meta
+
+    ws, qws = da.Workspace(), da.Workspace()
+    idx = torch.empty((2, 8, budget // s), dtype=torch.int32, device=DEV)
+    out_d = torch.empty_like(q)
+    out_s = torch.empty_like(q)
+
+    def step(k, v, meta):
+        da.gqa_decode_attn(q, k, v, sl, k_new=kn, v_new=vn, out=out_d, workspace=ws)
+        da.quest_append_score_topk(q, k, v, meta, sl, kn, vn, page_size=s, budget_tokens=budget,
+                                   page_idx=idx, workspace=qws)
+        da.quest_sparse_decode_attn(q, k, v, sl, idx, budget_tokens=budget, page_size=s,
+                                    out=out_s, workspace=ws)
+
+    k, v, meta = fresh()
+    step(k, v, meta)                       # eager reference (appends are idempotent)
+    torch.cuda.synchronize()
+    want = (host(out_d).copy(), host(out_s).copy(), host(idx).copy(), host(meta).copy())
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        step(k, v, meta)                   # warm-up on the capture stream
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            step(k, v, meta)
+    torch.cuda.synchronize()
+    noise = torch.randn(1 << 20, device=DEV)
+    for rep in range(4):
+        out_d.zero_()
+        out_s.zero_()
+        idx.fill_(-7)
+        noise.mul_(1.0001).add_(1.0)        # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (host(out_d), host(out_s), host(idx), host(meta))
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), rep
+
+
 def test_split_merge_reads_fresh_partials(da):
     """Calls alternate between different inputs and split counts on one
     workspace: every merge must see this call's partials, never the previous
