@@ -396,12 +396,9 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const uint64_t m = __ballot((take >> k) & 1);
-    const uint64_t c = __ballot((cand >> k) & 1);
     if (lane == 0) {
       selbits[k * 8 + 2 * wave] = (uint32_t)m;
       selbits[k * 8 + 2 * wave + 1] = (uint32_t)(m >> 32);
-      candbits[k * 8 + 2 * wave] = (uint32_t)c;
-      candbits[k * 8 + 2 * wave + 1] = (uint32_t)(c >> 32);
     }
   }
   __syncthreads();
@@ -409,8 +406,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
   if (need > 0 && need < ncand) {
     if (ncand <= (uint32_t)kMaxRankCand) {
       // exact ranking of the boundary candidates by (key desc, index asc):
-      // list them (slot order is irrelevant), then wave 0 holds one per lane
-      // and compares against every other through readlane
+      // list them in LDS (slot order is irrelevant), then rank each one
 #pragma unroll
       for (int k = 0; k < R; ++k) {
         if ((cand >> k) & 1) {
@@ -422,20 +418,36 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
         }
       }
       __syncthreads();
-      if (wave == 0) {
-        const bool has = lane < (int)ncand;
-        const uint32_t kc = has ? ckey[lane] : 0u;
-        const int ic = has ? cidx[lane] : 0x7FFFFFFF;
-        uint32_t rank = 0;
-        for (int j = 0; j < (int)ncand; ++j) {
-          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kc, j);
-          const int ij = __builtin_amdgcn_readlane(ic, j);
-          rank += (kj > kc) || (kj == kc && ij < ic);
-        }
-        if (has && rank < need) atomicOr(&selbits[ic >> 5], 1u << (ic & 31));
+      // four threads per candidate (a quad), each comparing it with a
+      // quarter of the list; the quad's counts add up through DPP
+      constexpr int kPerPart = kMaxRankCand / 4;
+      const int c = tid >> 2;
+      const int part = tid & 3;
+      const bool has = c < (int)ncand;
+      const uint32_t kc = has ? ckey[c] : 0u;
+      const int ic = has ? cidx[c] : 0x7FFFFFFF;
+      uint32_t rank = 0;
+#pragma unroll
+      for (int u = 0; u < kPerPart; ++u) {
+        const int j = part + 4 * u;
+        const uint32_t kj = ckey[j];
+        const int ij = cidx[j];
+        rank += (j < (int)ncand) && ((kj > kc) || (kj == kc && ij < ic));
       }
+      rank += dpp_u32<kDppXor1, 0xF, 0xF>(rank);
+      rank += dpp_u32<kDppXor2, 0xF, 0xF>(rank);
+      if (has && part == 0 && rank < need) atomicOr(&selbits[ic >> 5], 1u << (ic & 31));
     } else {
       // all key bits used and more equal keys than places: lowest indices win
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const uint64_t cb = __ballot((cand >> k) & 1);
+        if (lane == 0) {
+          candbits[k * 8 + 2 * wave] = (uint32_t)cb;
+          candbits[k * 8 + 2 * wave + 1] = (uint32_t)(cb >> 32);
+        }
+      }
+      __syncthreads();
       uint32_t mine = 0;
 #pragma unroll
       for (int q = 0; q < WPT; ++q) {
