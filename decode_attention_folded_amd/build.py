@@ -19,10 +19,13 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 HIP_SOURCES = ["decode_kernel.hip", "quest_kernels.hip", "repeat_kv.hip"]
 HOST_SOURCES = ["api.cpp"]
 
-# Packed-FP32 instructions are disabled for all device code.
+# Packed-FP32 instructions are disabled for all device code.  The kernels'
+# leading scalar arguments (at most 6) are preloaded into SGPRs at dispatch,
+# so their first loads do not wait for a read of the kernel-argument segment.
 DEVICE_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=6",
     "-Wall", "-Wno-unused-function",
 ]
 

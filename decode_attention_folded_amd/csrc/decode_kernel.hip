@@ -87,9 +87,10 @@ struct StreamInfo {
   int nsplit;   // splits with at least one key
 };
 
-__device__ __forceinline__ StreamInfo stream_info(const AttnLaunch& a, int b, bool sparse) {
+__device__ __forceinline__ StreamInfo stream_info(const AttnLaunch& a, const int32_t* seqlens, int b,
+                                                  bool sparse) {
   StreamInfo si;
-  const int L = a.seqlens[b];
+  const int L = seqlens[b];
   si.L = L < 0 ? 0 : (L > a.capacity ? a.capacity : L);
   si.n_keys = si.L;
   if (sparse) {
@@ -126,12 +127,13 @@ struct Stage {
 // valid length).  Splits past the valid ones are dropped by selects, so stale
 // workspace contents never enter the sums.
 template <int D, int G, int NT, typename NSplitFn>
-__device__ __forceinline__ void merge_partials(const AttnLaunch& a, int64_t unit,
+__device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float* part_ml,
+                                               const float* part_o, int max_splits, int64_t unit,
                                                NSplitFn get_nsplit) {
   constexpr int kIters = (G * D + NT - 1) / NT;  // output elements per thread
   constexpr int kBatch = 32 / kIters;            // splits per load batch
-  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + unit * a.max_splits * G;
-  const float* po = a.part_o + unit * a.max_splits * G * D;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + unit * max_splits * G;
+  const float* po = part_o + unit * max_splits * G * D;
   f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;
 
   float M[kIters], O[kIters], S[kIters];
@@ -151,7 +153,7 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, int64_t unit
       const int g = i / D;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int sp = min(s0 + u, a.max_splits - 1);
+        const int sp = min(s0 + u, max_splits - 1);
         mv[it][u] = ml[sp * G + g];
         ov[it][u] = po[(int64_t)sp * G * D + i];
       }
@@ -186,8 +188,13 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, int64_t unit
   }
 }
 
+// The leading scalar arguments repeat the fields of `a` that the first
+// instructions need (see `launch_one`); the rest of `a` is read from the
+// kernel-argument segment while the valid-length load is in flight.
 template <int D, int G, bool PAGED, bool SPARSE, bool QK_MFMA>
-__global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
+__global__ void __launch_bounds__(kThreads)
+    decode_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
+                  void* v, int batch, int hkv, AttnLaunch a) {
   constexpr int NCK = Layout<D>::NCK;
   constexpr int NCV = Layout<D>::NCV;
   constexpr int NV = Layout<D>::NV;
@@ -207,9 +214,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   const int rv = lane & 7;         // V key slots rv, rv + 8
   const int cv = lane >> 3;        // V chunk group (0..7)
   const bool upper = (lane & 8) != 0;
-  const int hkv = a.num_kv_heads;
   // grid < 2^31 workgroups (checked on the host): 32-bit index arithmetic
-  const uint32_t n_units = (uint32_t)a.batch * (uint32_t)hkv;
+  const uint32_t n_units = (uint32_t)batch * (uint32_t)hkv;
   const uint32_t split_u = blockIdx.x / n_units;
   const uint32_t unit_u = blockIdx.x - split_u * n_units;
   const uint32_t b_u = unit_u / (uint32_t)hkv;
@@ -226,7 +232,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
   // Inputs that do not depend on the valid length: the folded queries and the
   // raw page-list entries of the whole chunk (clamped indices; checked once
   // the length is known).
-  const f16* qb = reinterpret_cast<const f16*>(a.q) + unit * G * D;
+  const f16* qb = reinterpret_cast<const f16*>(q) + unit * G * D;
   // MFMA A operand: row i of chain c is query g = (4c + i % 4) mod G; the lane
   // holds row lane % 16 over the k-slots of chunk 4j + ck.
   f16x8 qa[QK_MFMA ? GC : 1][QK_MFMA ? NCK : 1];
@@ -262,7 +268,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
       raw_phys[r] = a.page_table[(int64_t)b * a.max_pages + min(max(logical, 0), a.max_pages - 1)];
   }
 
-  const StreamInfo si = stream_info(a, b, SPARSE);
+  const StreamInfo si = stream_info(a, seqlens, b, SPARSE);
   const int L = si.L;
   const int n_keys = si.n_keys;
   const int nsplit = si.nsplit;
@@ -322,8 +328,8 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
     safe_off = unit * a.cache_stride * D;
   }
 
-  const f16* kc = reinterpret_cast<const f16*>(a.k);
-  const f16* vc = reinterpret_cast<const f16*>(a.v);
+  const f16* kc = reinterpret_cast<const f16*>(k);
+  const f16* vc = reinterpret_cast<const f16*>(v);
   const bool has_new = a.k_new != nullptr;
   const f16* knew_row = has_new ? reinterpret_cast<const f16*>(a.k_new) + unit * D : nullptr;
   const f16* vnew_row = has_new ? reinterpret_cast<const f16*>(a.v_new) + unit * D : nullptr;
@@ -360,7 +366,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
     if (off >= 0 && threadIdx.x < 2 * (D / 8)) {
       const int c16 = threadIdx.x % (D / 8);
       const f16* src = (threadIdx.x < D / 8 ? knew_row : vnew_row) + 8 * c16;
-      f16* dst = reinterpret_cast<f16*>(threadIdx.x < D / 8 ? a.k : a.v) + off + 8 * c16;
+      f16* dst = reinterpret_cast<f16*>(threadIdx.x < D / 8 ? k : v) + off + 8 * c16;
       *reinterpret_cast<f16x8*>(dst) = *reinterpret_cast<const f16x8*>(src);
     }
   }
@@ -571,12 +577,18 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(AttnLaunch a) {
 // Merge kernel: one workgroup per (b, kv) unit, one thread per output element
 // of the unit's G rows (G * D threads, 64 to 1024), so every thread merges a
 // batch of up to 32 splits with one round of loads.
+// Leading scalar arguments as in the attention kernel: what the first batch
+// of partial loads needs.
 template <int D, int G>
-__global__ void __launch_bounds__(G * D) merge_kernel(AttnLaunch a, bool sparse) {
+__global__ void __launch_bounds__(G * D)
+    merge_kernel(const float* __restrict__ part_ml, const float* __restrict__ part_o,
+                 const int32_t* __restrict__ seqlens, int max_splits, int hkv, AttnLaunch a,
+                 bool sparse) {
   const int kv = blockIdx.x;
   const int b = blockIdx.y;
-  const int64_t unit = (int64_t)b * a.num_kv_heads + kv;
-  merge_partials<D, G, G * D>(a, unit, [&] { return stream_info(a, b, sparse).nsplit; });
+  const int64_t unit = (int64_t)b * hkv + kv;
+  merge_partials<D, G, G * D>(a, part_ml, part_o, max_splits, unit,
+                              [&] { return stream_info(a, seqlens, b, sparse).nsplit; });
 }
 
 template <int D, int G, bool PAGED, bool SPARSE>
@@ -584,15 +596,16 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
   const dim3 grid((uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads);
   if (a.qk_mfma) {
     hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, true>), grid, dim3(kThreads), 0,
-                       stream, a);
+                       stream, a.seqlens, a.q, a.k, a.v, a.batch, a.num_kv_heads, a);
   } else {
     hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, false>), grid, dim3(kThreads), 0,
-                       stream, a);
+                       stream, a.seqlens, a.q, a.k, a.v, a.batch, a.num_kv_heads, a);
   }
   const int err = (int)hipGetLastError();
   if (err != 0 || a.max_splits <= 1) return err;
   hipLaunchKernelGGL((merge_kernel<D, G>), dim3(a.num_kv_heads, a.batch), dim3(G * D), 0,
-                     stream, a, SPARSE);
+                     stream, a.part_ml, a.part_o, a.seqlens, a.max_splits, a.num_kv_heads, a,
+                     SPARSE);
   return (int)hipGetLastError();
 }
 

@@ -79,13 +79,15 @@ struct ScoreLaunch {
   int32_t score_passes;      // set by the launcher
   // Fused decode-step append (k_new != nullptr): row min(L_b, capacity) - 1 of
   // the cache receives k_new / v_new and its page's metadata is updated (reset
-  // at a page start, min/max otherwise) before the page is scored.
+  // at a page start, min/max otherwise) before the page is scored.  (The
+  // scalars come first: they share a kernel-argument cache line with the
+  // fields above.)
+  int32_t capacity, cache_stride, max_pages;
   const void* k_new;         // fp16 [B, Hkv, D] or nullptr
   const void* v_new;
   void* k;                   // cache or pool (written only with k_new)
   void* v;
   const int32_t* page_table; // [B, max_pages] or nullptr (contiguous cache)
-  int32_t capacity, cache_stride, max_pages;
   int64_t num_pages;
 };
 int launch_score_topk(const ScoreLaunch& p, void* stream);

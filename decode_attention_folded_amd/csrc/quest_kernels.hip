@@ -117,7 +117,12 @@ struct ScoreShape {
 // them with the group's per-channel sums of non-negative / negative queries,
 // and the D/8 lanes of a page add up their partial sums (DPP).
 template <int D, int G>
-__global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLaunch a) {
+// The leading scalar arguments repeat the fields of `a` that the first
+// instructions need (see `launch_score_topk`); the rest of `a` is read from
+// the kernel-argument segment while the valid-length load is in flight.
+__global__ void __launch_bounds__(kWave * kScoreWaves)
+    page_score_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q,
+                      void* meta, const void* __restrict__ k_new, int hkv, ScoreLaunch a) {
   using SS = ScoreShape<D>;
   constexpr int LPP = SS::LPP;
   constexpr int PPI = SS::PPI;
@@ -127,20 +132,40 @@ __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLa
   const int ch = lane % LPP;    // 16-byte chunk of the D channels
   const int kv = blockIdx.y;
   const int b = blockIdx.z;
-  const int64_t unit = (int64_t)b * a.num_kv_heads + kv;
+  const int64_t unit = (int64_t)b * hkv + kv;
   const int shift = a.page_shift;
 
-  int L = a.seqlens[b];
+  int L = seqlens[b];
   L = L < 0 ? 0 : L;
   int n_pages = (L + (1 << shift) - 1) >> shift;
   if (n_pages > a.meta_max_pages) n_pages = a.meta_max_pages;
   const int wg_begin = blockIdx.x * SS::PAGES_PER_PASS * a.score_passes;
   if (wg_begin >= n_pages) return;
 
+  // Metadata of one pass: kScoreDepth pages per lane slot; slots past the valid
+  // pages read page p0 (which exists) and store no score.  The first pass is
+  // requested here, before the query and append loads, so that all of them
+  // are in flight together; each later pass is requested after the previous
+  // one is scored.
+  f16* mbase = reinterpret_cast<f16*>(meta) + unit * a.meta_max_pages * 2 * D;
+  f16x8 mins[kScoreDepth], maxs[kScoreDepth];
+  int pg[kScoreDepth];
+  auto load_pass = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < kScoreDepth; ++u) {
+      const int p = p0 + (u * kScoreWaves + wave) * PPI + slot;
+      pg[u] = p;
+      const int64_t pp = p < n_pages ? p : p0;
+      mins[u] = stream_load(mbase + pp * 2 * D + 8 * ch);
+      maxs[u] = stream_load(mbase + pp * 2 * D + D + 8 * ch);
+    }
+  };
+  load_pass(wg_begin);
+
   // Per-channel weights: sum of the group's non-negative q_gi (pairs with the
   // max) and of its negative q_gi (pairs with the min).
   float wpos[8], wneg[8];
-  const f16* qb = reinterpret_cast<const f16*>(a.q) + unit * G * D + 8 * ch;
+  const f16* qb = reinterpret_cast<const f16*>(q) + unit * G * D + 8 * ch;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     wpos[e] = 0.0f;
@@ -159,35 +184,21 @@ __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLa
   // Fused append: the page holding the step's new key, its new min/max chunk.
   int p_app = -1;  // no lane matches when there is no append
   bool fresh = false;
-  f16x8 knew = {}, vnew = {};
+  f16x8 knew = {};
   int t_app = 0;
-  if (a.k_new != nullptr) {
-    int La = a.seqlens[b];
+  if (k_new != nullptr) {
+    int La = seqlens[b];
     La = La < 0 ? 0 : (La > a.capacity ? a.capacity : La);
     if (La >= 1) {
       t_app = La - 1;
       p_app = t_app >> shift;
       fresh = (t_app & ((1 << shift) - 1)) == 0;
-      knew = *reinterpret_cast<const f16x8*>(reinterpret_cast<const f16*>(a.k_new) + unit * D + 8 * ch);
-      vnew = *reinterpret_cast<const f16x8*>(reinterpret_cast<const f16*>(a.v_new) + unit * D + 8 * ch);
+      knew = *reinterpret_cast<const f16x8*>(reinterpret_cast<const f16*>(k_new) + unit * D + 8 * ch);
     }
   }
 
-  f16* mbase = reinterpret_cast<f16*>(a.meta) + unit * a.meta_max_pages * 2 * D;
   float* scores = a.scores + unit * a.meta_max_pages;
-  for (int pass = 0; pass < a.score_passes; ++pass) {
-    const int p0 = wg_begin + pass * SS::PAGES_PER_PASS;
-    if (p0 >= n_pages) break;
-    f16x8 mins[kScoreDepth], maxs[kScoreDepth];
-    int pg[kScoreDepth];
-#pragma unroll
-    for (int u = 0; u < kScoreDepth; ++u) {
-      const int p = p0 + (u * kScoreWaves + wave) * PPI + slot;
-      pg[u] = p;
-      const int64_t pp = p < n_pages ? p : p0;  // p0 exists; its score is not stored twice
-      mins[u] = stream_load(mbase + pp * 2 * D + 8 * ch);
-      maxs[u] = stream_load(mbase + pp * 2 * D + D + 8 * ch);
-    }
+  for (int pass = 0, p0 = wg_begin;;) {
     // the appended key enters its page's min/max before the page is scored
     // (selects, no branch: the wait counts of the loads stay exact)
     int app_u = -1;
@@ -225,16 +236,22 @@ __global__ void __launch_bounds__(kWave * kScoreWaves) page_score_kernel(ScoreLa
       if (a.page_table != nullptr) {
         const int phys = p_app < a.max_pages ? a.page_table[(int64_t)b * a.max_pages + p_app] : -1;
         if (phys >= 0 && phys < a.num_pages)
-          off = (((int64_t)phys * a.num_kv_heads + kv) << shift) * D +
+          off = (((int64_t)phys * hkv + kv) << shift) * D +
                 (int64_t)(t_app & ((1 << shift) - 1)) * D;
       } else {
         off = (unit * a.cache_stride + t_app) * D;
       }
-      if (off >= 0) {
+      if (off >= 0) {  // v_new is read only here, off the scoring path
+        const f16x8 vnew =
+            *reinterpret_cast<const f16x8*>(reinterpret_cast<const f16*>(a.v_new) + unit * D + 8 * ch);
         *reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(a.k) + off + 8 * ch) = knew;
         *reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(a.v) + off + 8 * ch) = vnew;
       }
     }
+    ++pass;
+    p0 += SS::PAGES_PER_PASS;
+    if (pass >= a.score_passes || p0 >= n_pages) break;
+    load_pass(p0);
   }
 }
 
@@ -263,8 +280,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 //      by (key descending, index ascending); if all 32 key bits are used up
 //      with more candidates, the lowest indices win;
 //   4. the bitmap is compacted in index order (ascending output, -1 pad).
+//
+// Leading scalar arguments as in the score kernel: the score row and its
+// width, so the score loads issue together with the valid-length load.
 template <int R>
-__global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
+__global__ void __launch_bounds__(kTopkThreads)
+    topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ seqlens, int hkv,
+                int row_pages, ScoreLaunch a) {
   static_assert(R >= 8 && R <= 64 && R % 8 == 0, "items per thread");
   constexpr int NW = R * kTopkThreads / 32;                      // bitmap words
   constexpr int WPT = (NW + kTopkThreads - 1) / kTopkThreads;    // words per thread
@@ -283,30 +305,36 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(ScoreLaunch a) {
   const int wave = tid / kWave;
   const int kv = blockIdx.x;
   const int b = blockIdx.y;
-  const int64_t unit = (int64_t)b * a.num_kv_heads + kv;
+  const int64_t unit = (int64_t)b * hkv + kv;
+  const float* sc = scores + unit * row_pages;
+  // The length and all score loads first, unconditionally, the scores at
+  // indices clamped to the row (not to the valid pages, which wait for the
+  // length), so they are in flight together; entries past the valid pages are
+  // masked below.  Relaxed workgroup-scope atomic loads are plain loads in the
+  // ISA; as atomics they keep their program order and are not sunk past the
+  // early exit below into the only path that reads them.
+  int L = __hip_atomic_load(seqlens + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  float raw[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k)
+    raw[k] = __hip_atomic_load(sc + min(k * kTopkThreads + tid, row_pages - 1), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+
   const int K = a.num_sel;
   int32_t* dst = a.page_idx + unit * K;
-
-  int L = a.seqlens[b];
   L = L < 0 ? 0 : L;
   int n_pages = (L + (1 << a.page_shift) - 1) >> a.page_shift;
-  if (n_pages > a.meta_max_pages) n_pages = a.meta_max_pages;
+  if (n_pages > row_pages) n_pages = row_pages;
   if (n_pages <= K) {  // every existing page is chosen
     for (int i = tid; i < K; i += kTopkThreads) dst[i] = i < n_pages ? i : -1;
     return;
   }
 
   if (tid == 0) n_listed = 0;  // ordered before its use by the barriers below
-  const float* sc = a.scores + unit * a.meta_max_pages;
   uint32_t key[R];
   uint64_t cand = 0;   // bit k: item k is still a candidate
   uint64_t take = 0;   // bit k: item k is chosen
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  // All loads first, unconditionally (clamped index), so they are in flight
-  // together; a load under the validity test would wait for each in turn.
-  float raw[R];
-#pragma unroll
-  for (int k = 0; k < R; ++k) raw[k] = sc[min(k * kTopkThreads + tid, n_pages - 1)];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const bool valid = k * kTopkThreads + tid < n_pages;
@@ -502,7 +530,8 @@ template <int D, int G>
 int launch_score(const ScoreLaunch& a, hipStream_t s) {
   const int per_wg = ScoreShape<D>::PAGES_PER_PASS * a.score_passes;
   dim3 grid((a.meta_max_pages + per_wg - 1) / per_wg, a.num_kv_heads, a.batch);
-  hipLaunchKernelGGL((page_score_kernel<D, G>), grid, dim3(kWave * kScoreWaves), 0, s, a);
+  hipLaunchKernelGGL((page_score_kernel<D, G>), grid, dim3(kWave * kScoreWaves), 0, s, a.seqlens,
+                     a.q, a.meta, a.k_new, a.num_kv_heads, a);
   return (int)hipGetLastError();
 }
 
@@ -520,7 +549,8 @@ int launch_score_d(const ScoreLaunch& a, hipStream_t s) {
 template <int R>
 int launch_topk(const ScoreLaunch& a, hipStream_t s) {
   dim3 grid(a.num_kv_heads, a.batch);
-  hipLaunchKernelGGL((topk_kernel<R>), grid, dim3(kTopkThreads), 0, s, a);
+  hipLaunchKernelGGL((topk_kernel<R>), grid, dim3(kTopkThreads), 0, s, a.scores, a.seqlens,
+                     a.num_kv_heads, a.meta_max_pages, a);
   return (int)hipGetLastError();
 }
 
