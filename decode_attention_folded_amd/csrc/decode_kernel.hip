@@ -143,10 +143,9 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
     O[it] = 0.0f;
     S[it] = 0.0f;
   }
-  int nsplit = 0;
-  for (int s0 = 0;; s0 += kBatch) {
-    float2 mv[kIters][kBatch];
-    float ov[kIters][kBatch];
+  float2 mv[kIters][kBatch];
+  float ov[kIters][kBatch];
+  auto load_batch = [&](int s0, auto load) {
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       const int i = min((int)threadIdx.x + it * NT, G * D - 1);
@@ -154,14 +153,12 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int sp = min(s0 + u, max_splits - 1);
-        mv[it][u] = ml[sp * G + g];
-        ov[it][u] = po[(int64_t)sp * G * D + i];
+        mv[it][u] = load(ml + sp * G + g);
+        ov[it][u] = load(po + (int64_t)sp * G * D + i);
       }
     }
-    if (s0 == 0) {
-      nsplit = get_nsplit();
-      if (nsplit <= 1) return;  // the attention kernel wrote the output
-    }
+  };
+  auto add_batch = [&](int s0, int nsplit) {
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       float bm = M[it];
@@ -179,7 +176,17 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
       O[it] = o;
       S[it] = l;
     }
-    if (s0 + kBatch >= nsplit) break;
+  };
+  // The first batch is issued before anything else (its addresses need only
+  // the leading arguments, and early loads are not moved past the exit
+  // below); later batches follow one by one.
+  load_batch(0, [](const auto* p) { return early_load(p); });
+  const int nsplit = get_nsplit();
+  if (nsplit <= 1) return;  // the attention kernel wrote the output
+  add_batch(0, nsplit);
+  for (int s0 = kBatch; s0 < nsplit; s0 += kBatch) {
+    load_batch(s0, [](const auto* p) { return *p; });
+    add_batch(s0, nsplit);
   }
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
@@ -579,16 +586,15 @@ __global__ void __launch_bounds__(kThreads)
 // batch of up to 32 splits with one round of loads.
 // Leading scalar arguments as in the attention kernel: what the first batch
 // of partial loads needs.
-template <int D, int G>
+template <int D, int G, bool SPARSE>
 __global__ void __launch_bounds__(G * D)
     merge_kernel(const float* __restrict__ part_ml, const float* __restrict__ part_o,
-                 const int32_t* __restrict__ seqlens, int max_splits, int hkv, AttnLaunch a,
-                 bool sparse) {
+                 const int32_t* __restrict__ seqlens, int max_splits, int hkv, AttnLaunch a) {
   const int kv = blockIdx.x;
   const int b = blockIdx.y;
   const int64_t unit = (int64_t)b * hkv + kv;
   merge_partials<D, G, G * D>(a, part_ml, part_o, max_splits, unit,
-                              [&] { return stream_info(a, seqlens, b, sparse).nsplit; });
+                              [&] { return stream_info(a, seqlens, b, SPARSE).nsplit; });
 }
 
 template <int D, int G, bool PAGED, bool SPARSE>
@@ -603,9 +609,8 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
   }
   const int err = (int)hipGetLastError();
   if (err != 0 || a.max_splits <= 1) return err;
-  hipLaunchKernelGGL((merge_kernel<D, G>), dim3(a.num_kv_heads, a.batch), dim3(G * D), 0,
-                     stream, a.part_ml, a.part_o, a.seqlens, a.max_splits, a.num_kv_heads, a,
-                     SPARSE);
+  hipLaunchKernelGGL((merge_kernel<D, G, SPARSE>), dim3(a.num_kv_heads, a.batch), dim3(G * D), 0,
+                     stream, a.part_ml, a.part_o, a.seqlens, a.max_splits, a.num_kv_heads, a);
   return (int)hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace da {
 
 typedef _Float16 f16;
@@ -69,6 +71,20 @@ __device__ __forceinline__ float lane_xor(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A load that stays where it is written: a relaxed workgroup-scope atomic
+// compiles to an ordinary global load, but keeps its program order with the
+// other such loads and is not sunk past a branch into the only path that uses
+// it.  For the first loads of a kernel, so that they are in flight before
+// anything waits for the rest of the kernel arguments.
+template <typename T>
+__device__ __forceinline__ T early_load(const T* p) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  using U = typename std::conditional<sizeof(T) == 4, uint32_t, uint64_t>::type;
+  const U u = __hip_atomic_load(reinterpret_cast<const U*>(p), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_bit_cast(T, u);
+}
 
 // 16-byte load with the non-temporal hint, for data read exactly once.
 __device__ __forceinline__ f16x8 stream_load(const f16* p) {

@@ -310,15 +310,11 @@ __global__ void __launch_bounds__(kTopkThreads)
   // The length and all score loads first, unconditionally, the scores at
   // indices clamped to the row (not to the valid pages, which wait for the
   // length), so they are in flight together; entries past the valid pages are
-  // masked below.  Relaxed workgroup-scope atomic loads are plain loads in the
-  // ISA; as atomics they keep their program order and are not sunk past the
-  // early exit below into the only path that reads them.
-  int L = __hip_atomic_load(seqlens + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // masked below.  Early loads are not moved past the exit below.
+  int L = early_load(seqlens + b);
   float raw[R];
 #pragma unroll
-  for (int k = 0; k < R; ++k)
-    raw[k] = __hip_atomic_load(sc + min(k * kTopkThreads + tid, row_pages - 1), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (int k = 0; k < R; ++k) raw[k] = early_load(sc + min(k * kTopkThreads + tid, row_pages - 1));
 
   const int K = a.num_sel;
   int32_t* dst = a.page_idx + unit * K;
