@@ -711,6 +711,35 @@ MAKERS = {
 }
 
 
+CAL_BYTES = 4 << 30
+
+
+def read_calibration(da, torch, dev, flush, reps=10):
+    """HBM read rate of the library's streaming-read calibration kernel over a
+    4 GiB buffer (cache flushed before each rep, median): the practical read
+    ceiling on this part, reported next to the nominal peak."""
+    buf = torch.full((CAL_BYTES,), 0x5A, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(reps + 2):
+        if flush is not None:
+            flush.zero_()
+        a.record()
+        da.read_calibration(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(a.elapsed_time(b) * 1e-3)
+    del buf, sink
+    torch.cuda.empty_cache()
+    sec = statistics.median(times)
+    return {"read_gbs": round(CAL_BYTES / sec / 1e9, 1), "bytes": CAL_BYTES,
+            "kernel": "read_calibration_kernel (da_read_calibration)",
+            "pct_of_peak": round(100 * CAL_BYTES / sec / 1e9 / HBM_PEAK_GBS, 2)}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -794,6 +823,7 @@ def main():
     del src, dst
 
     traffic = counter_traffic(args.workload)
+    cal = read_calibration(da, torch, dev, flush)
     line = {
         "metric": "decode-attn KV GB/s (% HBM peak) + us/step",
         "value": round(r["gbs"], 3),
@@ -815,6 +845,7 @@ def main():
             "unit": "GB/s",
             "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "frac_of_calibration": round(r["achieved"] / cal["read_gbs"], 4),
             "kernel": r["dominant"].kernels,
             "stage": r["dominant"].name,
             "calls_per_step": len(r["dominant"].fns),
@@ -836,12 +867,16 @@ def main():
                    else "the step's calls launched directly on the stream"),
         "timed_wall_s": r["timed_wall_s"],
         "stage_us": r["stage_us"],
+        "calibration": cal,
     }
     for key in ("dense_same_shape_us", "dense_same_shape_gbs", "dense_same_shape_pct_peak",
                 "quest_over_dense_time", "byte_model", "step_us_separate_append",
                 "us_per_step_graph"):
         if key in r:
             line[key] = r[key]
+    if "dense_same_shape_gbs" in r:
+        line["dense_same_shape_pct_calibration"] = round(
+            100 * r["dense_same_shape_gbs"] / cal["read_gbs"], 2)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step, data, args.seed)
@@ -863,6 +898,8 @@ def main():
             "dense_same_shape_us": q["dense_same_shape_us"],
             "dense_same_shape_gbs": q["dense_same_shape_gbs"],
             "dense_same_shape_pct_peak": q["dense_same_shape_pct_peak"],
+            "dense_same_shape_pct_calibration": round(
+                100 * q["dense_same_shape_gbs"] / cal["read_gbs"], 2),
             "quest_over_dense_time": q["quest_over_dense_time"],
             "byte_model_ratio": q["byte_model"]["ratio_model"],
         }

@@ -15,6 +15,7 @@ Entry points (same names as the C ABI):
 * :func:`quest_append_score_topk`  -- the step's append fused into scoring + top-K
 * :func:`quest_sparse_decode_attn` -- attention over the selected pages
 * :func:`gqa_repeat_kv`            -- the materialised repeat_kv copy (A/B baseline)
+* :func:`read_calibration`         -- streaming-read calibration (measurement helper)
 """
 
 _EXPORTS = (
@@ -25,6 +26,7 @@ _EXPORTS = (
     "quest_append_score_topk",
     "quest_sparse_decode_attn",
     "gqa_repeat_kv",
+    "read_calibration",
     "workspace_bytes",
     "quest_workspace_bytes",
     "Workspace",

@@ -28,7 +28,7 @@ STATUS_NAMES = {
 EXPORTED_SYMBOLS = (
     "da_status_string", "da_workspace_size", "gqa_decode_attn", "quest_meta_append",
     "da_quest_workspace_size", "quest_page_score_topk", "quest_sparse_decode_attn",
-    "gqa_repeat_kv", "quest_append_score_topk", "gqa_decode_attn_multi",
+    "gqa_repeat_kv", "quest_append_score_topk", "gqa_decode_attn_multi", "da_read_calibration",
 )
 
 
@@ -90,6 +90,7 @@ def load_library():
         lib.gqa_repeat_kv.argtypes = [KVP, I32, P, P, P, P]
         lib.quest_append_score_topk.argtypes = [P, KVP, P, I32, P, I32, I32, P, P, P, P, P, SZ,
                                                 P]
+        lib.da_read_calibration.argtypes = [P, SZ, P, P]
         for name in EXPORTED_SYMBOLS[1:]:
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
@@ -308,6 +309,21 @@ def gqa_repeat_kv(k_cache, v_cache, seqlens, num_q_heads, *, page_table=None, pa
                              _ptr(outs[1]), _stream_handle(k_cache.device, stream)),
            "gqa_repeat_kv")
     return outs[0], outs[1]
+
+
+def read_calibration(buf, sink, stream=None):
+    """Streaming-read calibration (``da_read_calibration``): reads every byte
+    of the contiguous device tensor ``buf`` once; ``sink`` is a device tensor
+    of at least 4 bytes.  A measurement helper: time it with events."""
+    lib = load_library()
+    for t, name in ((buf, "buf"), (sink, "sink")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    _check(lib.da_read_calibration(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                   _stream_handle(buf.device, stream)),
+           "da_read_calibration")
 
 
 def quest_meta_append(k_cache, v_cache, meta, seqlens, n_new=1, *, page_size, k_new=None,

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libdecode_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-HIP_SOURCES = ["decode_kernel.hip", "quest_kernels.hip", "repeat_kv.hip"]
+HIP_SOURCES = ["decode_kernel.hip", "quest_kernels.hip", "repeat_kv.hip", "calibrate.hip"]
 HOST_SOURCES = ["api.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code.  The kernels'

@@ -456,4 +456,11 @@ int quest_append_score_topk(const void* q, const da_kv_cache* kv, void* meta,
   return da::launch_score_topk(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
 }
 
+int da_read_calibration(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr) return DA_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return DA_ERR_SHAPE;
+  return da::launch_read_calibration(buf, bytes, sink, stream) == 0 ? DA_OK : DA_ERR_HIP;
+}
+
 }  // extern "C"

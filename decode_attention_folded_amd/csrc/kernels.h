@@ -110,4 +110,7 @@ struct RepeatLaunch {
 int launch_repeat_kv(const RepeatLaunch& p, void* stream);
 int repeat_kv_rows_per_workgroup();
 
+// Streaming-read calibration over `bytes` (a multiple of 16) at `src`.
+int launch_read_calibration(const void* src, uint64_t bytes, uint32_t* sink, void* stream);
+
 }  // namespace da

@@ -268,6 +268,22 @@ int quest_sparse_decode_attn(const void* q, const da_kv_cache* kv, const int32_t
                              int32_t num_q_heads, float scale, void* out, void* workspace,
                              size_t workspace_bytes, int32_t num_splits, void* stream);
 
+/*
+ * Measurement helper, not part of the method: the HBM read rate a plain
+ * streaming kernel reaches, the practical ceiling next to the nominal peak
+ * for kernels that stream K/V or page metadata.  Reads the `bytes` bytes at
+ * `buf` once with coalesced 16-byte non-temporal loads and folds them with
+ * XOR; `sink` receives one uint32 only if the fold equals a fixed constant
+ * (so the reads cannot be elided), and is otherwise left untouched.
+ *   buf   (device) any contents, 16-byte aligned
+ *   bytes > 0, a multiple of 16
+ *   sink  (device) uint32 [1]
+ * Asynchronous on `stream`; time it with events on that stream.
+ * Returns DA_ERR_NULL (buf or sink NULL), DA_ERR_SHAPE (bytes not a positive
+ * multiple of 16, or buf misaligned) or DA_ERR_HIP.
+ */
+int da_read_calibration(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,15 @@ def test_multi_query_validation_codes(lib):
     assert call(desc=_desc(batch=0), q=0, out=0) == 0
 
 
+def test_read_calibration_validation_codes(lib):
+    P = ctypes.c_void_p
+    assert lib.da_read_calibration(P(0), 1 << 20, P(FAKE), None) == -1
+    assert lib.da_read_calibration(P(FAKE), 1 << 20, P(0), None) == -1
+    assert lib.da_read_calibration(P(FAKE), 0, P(FAKE), None) == -2
+    assert lib.da_read_calibration(P(FAKE), 1000, P(FAKE), None) == -2
+    assert lib.da_read_calibration(P(FAKE + 8), 1 << 20, P(FAKE), None) == -2
+
+
 def test_status_strings(lib):
     for code in range(0, -7, -1):
         s = lib.da_status_string(code).decode()
