@@ -20,12 +20,12 @@ HIP_SOURCES = ["decode_kernel.hip", "quest_kernels.hip", "repeat_kv.hip", "calib
 HOST_SOURCES = ["api.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code.  The kernels'
-# leading scalar arguments (at most 6) are preloaded into SGPRs at dispatch,
+# leading scalar arguments (at most 9) are preloaded into SGPRs at dispatch,
 # so their first loads do not wait for a read of the kernel-argument segment.
 DEVICE_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-kernarg-preload-count=6",
+    "-mllvm", "-amdgpu-kernarg-preload-count=9",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -197,11 +197,16 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
 
 // The leading scalar arguments repeat the fields of `a` that the first
 // instructions need (see `launch_one`); the rest of `a` is read from the
-// kernel-argument segment while the valid-length load is in flight.
+// kernel-argument segment while the valid-length load is in flight.  `list`
+// is the first page list the chunk reads (the chosen pages, else the page
+// table, else unused) and `list_width` its row width; `chunk_geom` packs the
+// key tiles per chunk (bits 0-15) and log2 of the page size (bits 16 and up),
+// which place the chunk's list entries.
 template <int D, int G, bool PAGED, bool SPARSE, bool QK_MFMA>
 __global__ void __launch_bounds__(kThreads)
     decode_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
-                  void* v, int batch, int hkv, AttnLaunch a) {
+                  void* v, const int32_t* __restrict__ list, int batch, int hkv, int list_width,
+                  int chunk_geom, AttnLaunch a) {
   constexpr int NCK = Layout<D>::NCK;
   constexpr int NCV = Layout<D>::NCV;
   constexpr int NV = Layout<D>::NV;
@@ -230,9 +235,10 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t unit = unit_u;
   const int b = (int)b_u;
   const int kv = (int)(unit_u - b_u * (uint32_t)hkv);
-  const int shift = a.page_shift;
+  const int tiles_per_split = chunk_geom & 0xFFFF;
+  const int shift = chunk_geom >> 16;
   const int page_mask = (1 << shift) - 1;
-  const int tile_begin = split * a.tiles_per_split;
+  const int tile_begin = split * tiles_per_split;
   const int key_begin = tile_begin * kTileKeys;
   const int page0 = key_begin >> shift;
 
@@ -262,17 +268,29 @@ __global__ void __launch_bounds__(kThreads)
   }
   // Entry i of the chunk's page list: the chosen logical page (selected-page
   // stream) and/or the physical page (paged cache), read with clamped indices.
+  // The chosen pages are read with early loads, ahead of the valid-length
+  // wait.  (The page table of a dense paged stream is left to the compiler,
+  // which issues it after the wait: early loads there measured 2% slower on
+  // the var-length batch, where half of the workgroups have no keys.)
   constexpr int kListIters = (PAGED || SPARSE) ? (kMaxChunkPages + kThreads - 1) / kThreads : 0;
   int raw_logical[kListIters > 0 ? kListIters : 1];
   int raw_phys[kListIters > 0 ? kListIters : 1];
+  const int32_t* list_row =
+      (PAGED || SPARSE) ? list + (SPARSE ? unit : (int64_t)b) * list_width : nullptr;
 #pragma unroll
   for (int r = 0; r < kListIters; ++r) {
-    const int i = (int)threadIdx.x + r * kThreads;
-    int logical = page0 + i;
-    if constexpr (SPARSE) logical = a.page_idx[unit * a.num_sel + min(page0 + i, a.num_sel - 1)];
-    raw_logical[r] = logical;
-    if constexpr (PAGED)
-      raw_phys[r] = a.page_table[(int64_t)b * a.max_pages + min(max(logical, 0), a.max_pages - 1)];
+    const int e = min(page0 + (int)threadIdx.x + r * kThreads, list_width - 1);
+    if constexpr (SPARSE) {
+      raw_logical[r] = early_load(list_row + e);
+    } else {
+      raw_logical[r] = page0 + (int)threadIdx.x + r * kThreads;
+      if constexpr (PAGED) raw_phys[r] = list_row[e];
+    }
+  }
+  if constexpr (PAGED && SPARSE) {
+#pragma unroll
+    for (int r = 0; r < kListIters; ++r)
+      raw_phys[r] = a.page_table[(int64_t)b * a.max_pages + min(max(raw_logical[r], 0), a.max_pages - 1)];
   }
 
   const StreamInfo si = stream_info(a, seqlens, b, SPARSE);
@@ -290,7 +308,7 @@ __global__ void __launch_bounds__(kThreads)
   }
 
   const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
-  const int tile_end = min(tile_begin + a.tiles_per_split, n_tiles);
+  const int tile_end = min(tile_begin + tiles_per_split, n_tiles);
   const int key_last = min(tile_end * kTileKeys, n_keys) - 1;
 
   // Page lists of this chunk into LDS: the physical page of each logical page
@@ -599,13 +617,18 @@ __global__ void __launch_bounds__(G * D)
 
 template <int D, int G, bool PAGED, bool SPARSE>
 int launch_one(const AttnLaunch& a, hipStream_t stream) {
+  const int32_t* list = SPARSE ? a.page_idx : a.page_table;
+  const int list_width = SPARSE ? a.num_sel : (PAGED ? a.max_pages : 1);
+  const int chunk_geom = a.tiles_per_split | (a.page_shift << 16);  // tiles <= kMaxTilesPerSplit
   const dim3 grid((uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads);
   if (a.qk_mfma) {
     hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, true>), grid, dim3(kThreads), 0,
-                       stream, a.seqlens, a.q, a.k, a.v, a.batch, a.num_kv_heads, a);
+                       stream, a.seqlens, a.q, a.k, a.v, list, a.batch, a.num_kv_heads,
+                       list_width, chunk_geom, a);
   } else {
     hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, false>), grid, dim3(kThreads), 0,
-                       stream, a.seqlens, a.q, a.k, a.v, a.batch, a.num_kv_heads, a);
+                       stream, a.seqlens, a.q, a.k, a.v, list, a.batch, a.num_kv_heads,
+                       list_width, chunk_geom, a);
   }
   const int err = (int)hipGetLastError();
   if (err != 0 || a.max_splits <= 1) return err;
