@@ -404,20 +404,26 @@ __global__ void __launch_bounds__(kThreads)
     t = j;
     valid = live && j < n_keys;
     int64_t off;
+    // The list entries are read unconditionally (the index is in range
+    // either way) and masked afterwards, so the reads of a stage issue
+    // together instead of each behind a branch and a wait.
     if constexpr (SPARSE) {
       const int li = valid ? (j >> shift) - page0 : 0;  // in range of the LDS list
-      const int logical = valid ? s_page[li] : -1;
+      const int logical_raw = s_page[li];
+      const int phys_raw = PAGED ? s_phys[li] : 0;
+      const int logical = valid ? logical_raw : -1;
       t = (logical << shift) + (j & page_mask);
       valid = valid && logical >= 0 && t < L;
       if constexpr (PAGED) {
-        const int phys = valid ? s_phys[li] : -1;
+        const int phys = valid ? phys_raw : -1;
         valid = valid && phys >= 0;
         off = (((int64_t)phys * hkv + kv) << shift) * D + (int64_t)(t & page_mask) * D;
       } else {
         off = (unit * a.cache_stride + t) * D;
       }
     } else if constexpr (PAGED) {
-      const int phys = valid ? s_page[valid ? (j >> shift) - page0 : 0] : -1;
+      const int phys_raw = s_page[valid ? (j >> shift) - page0 : 0];
+      const int phys = valid ? phys_raw : -1;
       valid = valid && phys >= 0;
       off = (((int64_t)phys * hkv + kv) << shift) * D + (int64_t)(t & page_mask) * D;
     } else {
