@@ -20,7 +20,7 @@ constexpr int kMaxGridDim = 65535;
 // Split plan: enough key tiles per workgroup that the grid is about one
 // workgroup per CU (256 CUs), longer chunks where the stream allows.  Measured
 // against 384, 512, 768 and 1024: equal on the dense and paged workloads
-// (their chunks are at the 128-tile cap or the 8-tile floor) and best on the
+// (their chunks are at the chunk cap or the 8-tile floor) and best on the
 // 128K selected-page stream (34.4 us vs 35.2 at 512, 37.0 at 768, 40 at 384).
 constexpr int kTargetWorkgroups = 256;
 constexpr int kMinTilesPerSplit = 8;     // at least 2 tiles per wave
@@ -78,7 +78,8 @@ int check_cache(const da_kv_cache* kv, int32_t num_q_heads, Shape* s) {
   return DA_OK;
 }
 
-da::SplitPlan plan_splits(const Shape& s, int max_keys, int num_splits) {
+// page_list: the stream reads a page list (paged cache or chosen pages).
+da::SplitPlan plan_splits(const Shape& s, int max_keys, int num_splits, bool page_list) {
   da::SplitPlan p;
   p.keys_per_tile = da::keys_per_tile(s.d, s.group);
   const int64_t max_tiles = max_keys < 1 ? 1 : (max_keys + p.keys_per_tile - 1) / p.keys_per_tile;
@@ -91,7 +92,7 @@ da::SplitPlan plan_splits(const Shape& s, int max_keys, int num_splits) {
     if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
   }
   if (tps < 1) tps = 1;
-  if (tps > da::max_tiles_per_split()) tps = da::max_tiles_per_split();
+  if (tps > da::max_tiles_per_split(page_list)) tps = da::max_tiles_per_split(page_list);
   if (tps > max_tiles) tps = max_tiles;
   p.tiles_per_split = (int32_t)tps;
   p.max_splits = (int32_t)((max_tiles + tps - 1) / tps);
@@ -163,7 +164,7 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
       !aligned16(k_new) || !aligned16(v_new))
     return DA_ERR_SHAPE;
   const da::SplitPlan plan = plan_splits(s, max_stream_keys(s, page_idx ? budget_tokens : 0),
-                                         num_splits);
+                                         num_splits, s.paged || page_idx != nullptr);
   // one workgroup per (split, b, kv) on a 1-D grid
   if ((int64_t)plan.max_splits * s.batch * s.hkv > INT32_MAX) return DA_ERR_SHAPE;
   const WsLayout w = ws_layout(s, plan);
@@ -232,7 +233,8 @@ int da_workspace_size(const da_kv_cache* kv, int32_t num_q_heads, int32_t budget
   } else if (budget_tokens < 0) {
     return DA_ERR_BUDGET;
   }
-  const da::SplitPlan plan = plan_splits(s, max_stream_keys(s, budget_tokens), num_splits);
+  const da::SplitPlan plan = plan_splits(s, max_stream_keys(s, budget_tokens), num_splits,
+                                         s.paged || budget_tokens > 0);
   *bytes_out = ws_layout(s, plan).total;
   return DA_OK;
 }

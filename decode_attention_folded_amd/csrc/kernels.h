@@ -47,7 +47,7 @@ struct SplitPlan {
 };
 
 int keys_per_tile(int head_dim, int group);
-int max_tiles_per_split();
+int max_tiles_per_split(bool page_list);  // page_list: paged cache or chosen pages
 
 int launch_decode(const AttnLaunch& p, void* stream);
 
