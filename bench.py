@@ -56,8 +56,8 @@ FLUSH_BYTES = 1 << 30
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="exaone30",
                     choices=["exaone30", "gqa1", "paged", "quest32k", "quest128k",
                              "repeat_kv_ab", "quest_sweep", "multi_query"])
