@@ -298,7 +298,6 @@ __global__ void __launch_bounds__(kTopkThreads)
   __shared__ uint32_t candbits[NW];
   __shared__ uint32_t ckey[kMaxRankCand];
   __shared__ int32_t cidx[kMaxRankCand];
-  __shared__ uint32_t n_listed;
 
   const int tid = threadIdx.x;
   const int lane = lane_in_wave();
@@ -326,7 +325,6 @@ __global__ void __launch_bounds__(kTopkThreads)
     return;
   }
 
-  if (tid == 0) n_listed = 0;  // ordered before its use by the barriers below
   uint32_t key[R];
   uint64_t cand = 0;   // bit k: item k is still a candidate
   uint64_t take = 0;   // bit k: item k is chosen
@@ -430,15 +428,18 @@ __global__ void __launch_bounds__(kTopkThreads)
   if (need > 0 && need < ncand) {
     if (ncand <= (uint32_t)kMaxRankCand) {
       // exact ranking of the boundary candidates by (key desc, index asc):
-      // list them in LDS (slot order is irrelevant), then rank each one
+      // list them in LDS, each thread at the block prefix of its candidate
+      // count (plain stores; an LDS atomic per slot costs a round trip each),
+      // then rank each one
+      uint32_t listed_total;
+      uint32_t pos = block_exclusive_scan<kTopkWaves>((uint32_t)__builtin_popcountll(cand),
+                                                      scratch, &listed_total);
 #pragma unroll
       for (int k = 0; k < R; ++k) {
-        if ((cand >> k) & 1) {
-          const uint32_t pos = atomicAdd(&n_listed, 1u);
-          if (pos < (uint32_t)kMaxRankCand) {  // ncand <= 64 candidates exist
-            ckey[pos] = key[k];
-            cidx[pos] = k * kTopkThreads + tid;
-          }
+        if ((cand >> k) & 1) {  // ncand <= 64 candidates exist: pos < 64
+          ckey[pos] = key[k];
+          cidx[pos] = k * kTopkThreads + tid;
+          ++pos;
         }
       }
       __syncthreads();
