@@ -198,6 +198,22 @@ def quest(da, torch, seed, dev, long_ctx):
         da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx,
                                     budget_tokens=budget, page_size=s, out=out, workspace=ws)
 
+    # The step as launched by default: scores (with the step's append at 128K),
+    # then the top-K fused into the selected-page attention.
+    def append_score():
+        da.quest_append_score_topk(c["q"], c["k"], c["v"], meta, c["seqlens"], c["k_new"],
+                                   c["v_new"], page_size=s, budget_tokens=budget,
+                                   page_scores=scores, select=False)
+
+    def score():
+        da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s, budget_tokens=budget,
+                                 page_scores=scores, select=False)
+
+    def select_attend():
+        da.quest_select_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], scores,
+                                           budget_tokens=budget, page_size=s, page_idx=idx,
+                                           out=out, workspace=ws)
+
     def dense():
         da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], out=dense_out, workspace=dws)
 
@@ -207,27 +223,33 @@ def quest(da, torch, seed, dev, long_ctx):
     dense_bytes = units * L * 2 * d * 2
     kv_bytes = meta_bytes + sel_bytes
     qo_bytes = 2 * b * hq * d * 2
-    score_bytes = meta_bytes + 2 * units * P * 4 + units * k_sel * 4 + b * hq * d * 2
-    attend_bytes = sel_bytes + qo_bytes + units * k_sel * 4
+    # scores written by the score stage and read by the selecting attention;
+    # the chosen pages written by it
+    score_bytes = meta_bytes + units * P * 4 + b * hq * d * 2
+    attend_bytes = sel_bytes + qo_bytes + units * P * 4 + units * k_sel * 4
     # append: the new K/V row (read + write) and the touched page's min/max
     append_bytes = units * (2 * 2 * d * 2 + 2 * 2 * d * 2)
     algo = score_bytes + attend_bytes + (append_bytes if long_ctx else 0)
     if long_ctx:
-        stages = [Stage("append_score_topk", [append_select], score_bytes + append_bytes,
-                        "page_score_kernel (with the append) + topk_kernel "
-                        "(quest_append_score_topk)")]
+        stages = [Stage("append_score", [append_score], score_bytes + append_bytes,
+                        "page_score_kernel with the append (quest_append_score_topk, "
+                        "scores only)")]
     else:
-        stages = [Stage("score_topk", [select], score_bytes,
-                        "page_score_kernel + topk_kernel (quest_page_score_topk)")]
-    stages.append(Stage("sparse_attention", [attend], attend_bytes,
-                        "decode_kernel + merge_kernel (quest_sparse_decode_attn)"))
+        stages = [Stage("score", [score], score_bytes,
+                        "page_score_kernel (quest_page_score_topk, scores only)")]
+    stages.append(Stage("select_sparse_attention", [select_attend], attend_bytes,
+                        "decode_kernel selecting its pages + merge_kernel "
+                        "(quest_select_sparse_decode_attn)"))
     cfg = {"workload": name, "batch": b, "num_q_heads": hq, "num_kv_heads": hkv,
            "head_dim": d, "seq_len": L, "page_size": s, "budget_tokens": budget,
            "k_pages": k_sel}
     st = Step("quest128k" if long_ctx else "quest32k", cfg, kv_bytes, algo, stages)
     st.dense_fn = dense
-    if long_ctx:   # the same step with the append as its own launch, for comparison
-        st.separate_append_fns = [append, select, attend]
+    # the same step with the top-K as its own launch, and (128K) with the
+    # append as its own launch too, for comparison
+    st.variants = {"separate_topk": [append_select if long_ctx else select, attend]}
+    if long_ctx:
+        st.variants["separate_append"] = [append, select, attend]
     st.dense_bytes = dense_bytes
     st.byte_model = {"meta_bytes": meta_bytes, "selected_bytes": sel_bytes,
                      "dense_bytes": dense_bytes,
@@ -474,9 +496,8 @@ def measure(torch, da, dev, step, steps, warmup, flush):
         "timed_wall_s": round(t_wall, 3),
         "stage_us": {st.name: round(m * 1e3, 3) for st, m in zip(step.stages, med)},
     }
-    if hasattr(step, "separate_append_fns"):
-        sep_ms = statistics.median(run(step.separate_append_fns, steps, 2)[0])
-        res["step_us_separate_append"] = round(sep_ms * 1e3, 3)
+    for name, fns in getattr(step, "variants", {}).items():
+        res["step_us_" + name] = round(statistics.median(run(fns, steps, 2)[0]) * 1e3, 3)
     if hasattr(step, "dense_fn"):
         dense_ms = statistics.median(run([step.dense_fn], max(10, steps // 2), 2)[0])
         res["dense_same_shape_us"] = round(dense_ms * 1e3, 3)
@@ -870,8 +891,8 @@ def main():
         "calibration": cal,
     }
     for key in ("dense_same_shape_us", "dense_same_shape_gbs", "dense_same_shape_pct_peak",
-                "quest_over_dense_time", "byte_model", "step_us_separate_append",
-                "us_per_step_graph"):
+                "quest_over_dense_time", "byte_model", "step_us_separate_topk",
+                "step_us_separate_append", "us_per_step_graph"):
         if key in r:
             line[key] = r[key]
     if "dense_same_shape_gbs" in r:
@@ -892,6 +913,7 @@ def main():
         line["long_context"] = {
             "workload": qstep.config["workload"],
             "quest_us_per_step": q["us_per_step"],
+            "quest_us_per_step_separate_topk": q["step_us_separate_topk"],
             "quest_us_per_step_separate_append": q["step_us_separate_append"],
             "quest_kv_gbs": round(q["gbs"], 1),
             "stage_us": q["stage_us"],

@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
 * :func:`quest_page_score_topk`    -- page scores and top-K page selection
 * :func:`quest_append_score_topk`  -- the step's append fused into scoring + top-K
 * :func:`quest_sparse_decode_attn` -- attention over the selected pages
+* :func:`quest_select_sparse_decode_attn` -- top-K fused into that attention
 * :func:`gqa_repeat_kv`            -- the materialised repeat_kv copy (A/B baseline)
 * :func:`read_calibration`         -- streaming-read calibration (measurement helper)
 """
@@ -25,6 +26,7 @@ _EXPORTS = (
     "quest_page_score_topk",
     "quest_append_score_topk",
     "quest_sparse_decode_attn",
+    "quest_select_sparse_decode_attn",
     "gqa_repeat_kv",
     "read_calibration",
     "workspace_bytes",

@@ -29,6 +29,7 @@ EXPORTED_SYMBOLS = (
     "da_status_string", "da_workspace_size", "gqa_decode_attn", "quest_meta_append",
     "da_quest_workspace_size", "quest_page_score_topk", "quest_sparse_decode_attn",
     "gqa_repeat_kv", "quest_append_score_topk", "gqa_decode_attn_multi", "da_read_calibration",
+    "quest_select_sparse_decode_attn",
 )
 
 
@@ -91,6 +92,8 @@ def load_library():
         lib.quest_append_score_topk.argtypes = [P, KVP, P, I32, P, I32, I32, P, P, P, P, P, SZ,
                                                 P]
         lib.da_read_calibration.argtypes = [P, SZ, P, P]
+        lib.quest_select_sparse_decode_attn.argtypes = [P, KVP, P, P, I32, I32, I32, F32, P, P,
+                                                        P, SZ, I32, P]
         for name in EXPORTED_SYMBOLS[1:]:
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
@@ -349,11 +352,30 @@ def quest_meta_append(k_cache, v_cache, meta, seqlens, n_new=1, *, page_size, k_
     return meta
 
 
+def _page_idx_out(select, page_idx, page_scores, batch, hkv, budget_tokens, page_size, device):
+    """The chosen-page output of a scoring call: a tensor (allocated if not
+    given), or None for scores only (select=False)."""
+    if not select:
+        if page_scores is None:
+            raise ValueError("select=False needs page_scores (the scores are the only output)")
+        if page_idx is not None:
+            raise ValueError("select=False writes no page_idx")
+        return None
+    k_pages = budget_tokens // page_size if page_size > 0 else 0
+    if page_idx is None:
+        return torch.empty((batch, hkv, max(k_pages, 1)), dtype=torch.int32, device=device)
+    _need(page_idx, "page_idx", torch.int32, 3)
+    if tuple(page_idx.shape) != (batch, hkv, k_pages):
+        raise ValueError("page_idx must be [B, Hkv, budget_tokens / page_size]")
+    return page_idx
+
+
 def quest_page_score_topk(q, meta, seqlens, *, page_size, budget_tokens, page_idx=None,
-                          page_scores=None, workspace=None, stream=None):
+                          page_scores=None, workspace=None, select=True, stream=None):
     """Page scores and top-K chosen pages.  Returns page_idx [B, Hkv, K]
     int32 (ascending, -1 padded); fills page_scores [B, Hkv, P] fp32 if
-    given."""
+    given.  select=False: the scores only (page_scores required, returns
+    None), for quest_select_sparse_decode_attn."""
     lib = load_library()
     _need(q, "q", torch.float16, 3)
     _need(meta, "meta", torch.float16, 5)
@@ -364,13 +386,8 @@ def quest_page_score_topk(q, meta, seqlens, *, page_size, budget_tokens, page_id
         raise ValueError("meta must be [B, Hkv, P, 2, D] matching q")
     if seqlens.shape[0] != batch:
         raise ValueError("seqlens must be [B]")
-    k_pages = budget_tokens // page_size if page_size > 0 else 0
-    if page_idx is None:
-        page_idx = torch.empty((batch, hkv, max(k_pages, 1)), dtype=torch.int32, device=q.device)
-    else:
-        _need(page_idx, "page_idx", torch.int32, 3)
-        if tuple(page_idx.shape) != (batch, hkv, k_pages):
-            raise ValueError("page_idx must be [B, Hkv, budget_tokens / page_size]")
+    page_idx = _page_idx_out(select, page_idx, page_scores, batch, hkv, budget_tokens,
+                             page_size, q.device)
     ws = None
     if page_scores is None:
         ws = _workspace(workspace, q.device, "scores").get(
@@ -389,10 +406,12 @@ def quest_page_score_topk(q, meta, seqlens, *, page_size, budget_tokens, page_id
 
 def quest_append_score_topk(q, k_cache, v_cache, meta, seqlens, k_new, v_new, *, page_size,
                             budget_tokens, page_table=None, page_idx=None, page_scores=None,
-                            workspace=None, stream=None):
+                            workspace=None, select=True, stream=None):
     """One decode step's K/V row append and metadata update fused into page
     scoring and top-K (see ``quest_append_score_topk`` in decode_attn.h).
-    Updates the cache and meta in place; returns page_idx [B, Hkv, K] int32."""
+    Updates the cache and meta in place; returns page_idx [B, Hkv, K] int32
+    (select=False: the append and the scores only; page_scores required,
+    returns None)."""
     lib = load_library()
     _need(q, "q", torch.float16, 3)
     _need(meta, "meta", torch.float16, 5)
@@ -408,13 +427,8 @@ def quest_append_score_topk(q, k_cache, v_cache, meta, seqlens, k_new, v_new, *,
         if tuple(t.shape) != (batch, desc.num_kv_heads, d):
             raise ValueError(f"{name} must be [B, Hkv, D]")
     hkv, max_pages = desc.num_kv_heads, meta.shape[2]
-    k_pages = int(budget_tokens) // int(page_size) if page_size > 0 else 0
-    if page_idx is None:
-        page_idx = torch.empty((batch, hkv, max(k_pages, 1)), dtype=torch.int32, device=q.device)
-    else:
-        _need(page_idx, "page_idx", torch.int32, 3)
-        if tuple(page_idx.shape) != (batch, hkv, k_pages):
-            raise ValueError("page_idx must be [B, Hkv, budget_tokens / page_size]")
+    page_idx = _page_idx_out(select, page_idx, page_scores, batch, hkv, budget_tokens,
+                             page_size, q.device)
     ws = None
     if page_scores is None:
         ws = _workspace(workspace, q.device, "scores").get(
@@ -457,4 +471,40 @@ def quest_sparse_decode_attn(q, k_cache, v_cache, seqlens, page_idx, *, budget_t
                                         _ptr(ws), ws.numel(), num_splits,
                                         _stream_handle(q.device, stream)),
            "quest_sparse_decode_attn")
+    return out
+
+
+def quest_select_sparse_decode_attn(q, k_cache, v_cache, seqlens, page_scores, *, budget_tokens,
+                                    page_size, scale=None, page_table=None, page_idx=None,
+                                    out=None, workspace=None, num_splits=0, stream=None):
+    """Top-K page selection from page_scores [B, Hkv, P] fp32 fused into the
+    attention over the chosen pages (see ``quest_select_sparse_decode_attn`` in
+    decode_attn.h).  Returns out [B, Hq, D] fp16; fills page_idx [B, Hkv, K]
+    int32 with the choice if given."""
+    lib = load_library()
+    _need(q, "q", torch.float16, 3)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    _need(page_scores, "page_scores", torch.float32, 3)
+    batch, hq, d = q.shape
+    desc = _kv_desc(k_cache, v_cache, batch, page_table, page_size)
+    _check_common(q, seqlens, desc)
+    if tuple(page_scores.shape[:2]) != (batch, desc.num_kv_heads):
+        raise ValueError("page_scores must be [B, Hkv, P]")
+    if page_idx is not None:
+        _need(page_idx, "page_idx", torch.int32, 3)
+        if page_size > 0 and tuple(page_idx.shape) != (batch, desc.num_kv_heads,
+                                                       budget_tokens // page_size):
+            raise ValueError("page_idx must be [B, Hkv, budget_tokens / page_size]")
+    out = _out_like(q, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = ctypes.c_size_t()
+    _check(lib.da_workspace_size(ctypes.byref(desc), hq, budget_tokens, num_splits,
+                                 ctypes.byref(nbytes)), "da_workspace_size")
+    ws = _workspace(workspace, q.device).get(nbytes.value, q.device)
+    _check(lib.quest_select_sparse_decode_attn(_ptr(q), ctypes.byref(desc), _ptr(seqlens),
+                                               _ptr(page_scores), page_scores.shape[2],
+                                               budget_tokens, hq, scale, _ptr(page_idx),
+                                               _ptr(out), _ptr(ws), ws.numel(), num_splits,
+                                               _stream_handle(q.device, stream)),
+           "quest_select_sparse_decode_attn")
     return out

@@ -142,17 +142,27 @@ int check_budget(const Shape& s, int budget_tokens) {
 
 // num_rows = Hq * q_len: the kernel reads Q [B, Hq, q_len, D] as
 // [B, Hkv, G * q_len, D] rows.
+// Pages chosen inside the attention launch from the page scores (the
+// selected-page stream without a given page list).
+struct PageSelect {
+  const float* scores;  // [B, Hkv, row] fp32
+  int32_t row;          // pages with a score per (b, kv)
+  int32_t* idx_out;     // [B, Hkv, K] the choice, or nullptr
+};
+
 int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
                   const int32_t* page_idx, int32_t budget_tokens, int32_t num_rows,
                   int32_t q_len, float scale, const void* k_new, const void* v_new, void* out,
-                  void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream) {
+                  void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream,
+                  const PageSelect* select = nullptr) {
   Shape s;
   int st = check_cache(kv, num_rows, &s);
   if (st != DA_OK) return st;
   if ((k_new == nullptr) != (v_new == nullptr)) return DA_ERR_NULL;
   if (!isfinite(scale)) return DA_ERR_SHAPE;
   if (num_splits < 0) return DA_ERR_SHAPE;
-  if (page_idx != nullptr) {
+  const bool sparse = page_idx != nullptr || select != nullptr;
+  if (sparse) {
     st = check_budget(s, budget_tokens);
     if (st != DA_OK) return st;
   }
@@ -163,8 +173,8 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
   if (!aligned16(q) || !aligned16(out) || !aligned16(kv->k) || !aligned16(kv->v) ||
       !aligned16(k_new) || !aligned16(v_new))
     return DA_ERR_SHAPE;
-  const da::SplitPlan plan = plan_splits(s, max_stream_keys(s, page_idx ? budget_tokens : 0),
-                                         num_splits, s.paged || page_idx != nullptr);
+  const da::SplitPlan plan = plan_splits(s, max_stream_keys(s, sparse ? budget_tokens : 0),
+                                         num_splits, s.paged || sparse);
   // one workgroup per (split, b, kv) on a 1-D grid
   if ((int64_t)plan.max_splits * s.batch * s.hkv > INT32_MAX) return DA_ERR_SHAPE;
   const WsLayout w = ws_layout(s, plan);
@@ -192,10 +202,13 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
   a.head_dim = s.d;
   a.capacity = s.capacity;
   a.cache_stride = s.stride;
-  a.page_shift = (s.paged || page_idx) ? log2i(s.page_size) : 0;
+  a.page_shift = (s.paged || sparse) ? log2i(s.page_size) : 0;
   a.max_pages = s.max_pages;
   a.num_pages = kv->num_pages;
-  a.num_sel = page_idx ? budget_tokens / s.page_size : 0;
+  a.num_sel = sparse ? budget_tokens / s.page_size : 0;
+  a.sel_scores = select != nullptr ? select->scores : nullptr;
+  a.sel_row = select != nullptr ? select->row : 0;
+  a.sel_idx_out = select != nullptr ? select->idx_out : nullptr;
   a.tiles_per_split = plan.tiles_per_split;
   a.max_splits = plan.max_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -372,8 +385,8 @@ int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_page
   if (budget_tokens <= 0 || budget_tokens % page_size != 0) return DA_ERR_BUDGET;
   if (meta_max_pages > da::topk_max_pages()) return DA_ERR_UNSUPPORTED;
   if (batch == 0) return DA_OK;  // nothing to read or write
-  if (q == nullptr || meta == nullptr || seqlens == nullptr || page_idx == nullptr)
-    return DA_ERR_NULL;
+  if (q == nullptr || meta == nullptr || seqlens == nullptr) return DA_ERR_NULL;
+  if (page_idx == nullptr && page_scores == nullptr) return DA_ERR_NULL;  // nothing to output
   if (!aligned16(q) || !aligned16(meta)) return DA_ERR_SHAPE;
   float* scores = page_scores;
   if (scores == nullptr) {
@@ -423,9 +436,10 @@ int quest_append_score_topk(const void* q, const da_kv_cache* kv, void* meta,
     return DA_ERR_SHAPE;
   if (meta_max_pages > da::topk_max_pages()) return DA_ERR_UNSUPPORTED;
   if (s.batch == 0) return DA_OK;  // nothing to read or write
-  if (q == nullptr || meta == nullptr || seqlens == nullptr || page_idx == nullptr ||
-      k_new == nullptr || v_new == nullptr || kv->k == nullptr || kv->v == nullptr)
+  if (q == nullptr || meta == nullptr || seqlens == nullptr || k_new == nullptr ||
+      v_new == nullptr || kv->k == nullptr || kv->v == nullptr)
     return DA_ERR_NULL;
+  if (page_idx == nullptr && page_scores == nullptr) return DA_ERR_NULL;  // nothing to output
   if (!aligned16(q) || !aligned16(meta) || !aligned16(k_new) || !aligned16(v_new) ||
       !aligned16(kv->k) || !aligned16(kv->v))
     return DA_ERR_SHAPE;
@@ -461,6 +475,29 @@ int quest_append_score_topk(const void* q, const da_kv_cache* kv, void* meta,
   a.max_pages = s.max_pages;
   a.num_pages = kv->num_pages;
   return da::launch_score_topk(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
+}
+
+int quest_select_sparse_decode_attn(const void* q, const da_kv_cache* kv,
+                                    const int32_t* seqlens, const float* page_scores,
+                                    int32_t meta_max_pages, int32_t budget_tokens,
+                                    int32_t num_q_heads, float scale, int32_t* page_idx,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    int32_t num_splits, void* stream) {
+  Shape s;
+  int st = check_cache(kv, num_q_heads, &s);
+  if (st != DA_OK) return st;
+  st = check_budget(s, budget_tokens);
+  if (st != DA_OK) return st;
+  if (meta_max_pages < 1 || (int64_t)meta_max_pages * s.page_size < s.capacity)
+    return DA_ERR_SHAPE;  // every page that can hold a valid token has a score
+  if (meta_max_pages > da::topk_max_pages()) return DA_ERR_UNSUPPORTED;
+  if (s.batch > 0 && page_scores == nullptr) return DA_ERR_NULL;
+  PageSelect sel;
+  sel.scores = page_scores;
+  sel.row = meta_max_pages;
+  sel.idx_out = page_idx;
+  return run_attention(q, kv, seqlens, nullptr, budget_tokens, num_q_heads, 1, scale, nullptr,
+                       nullptr, out, workspace, workspace_bytes, num_splits, stream, &sel);
 }
 
 int da_read_calibration(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

@@ -62,6 +62,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace da {
 namespace {
@@ -204,15 +205,26 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
 // The leading scalar arguments repeat the fields of `a` that the first
 // instructions need (see `launch_one`); the rest of `a` is read from the
 // kernel-argument segment while the valid-length load is in flight.  `list`
-// is the first page list the chunk reads (the chosen pages, else the page
-// table, else unused) and `list_width` its row width; `chunk_geom` packs the
-// key tiles per chunk (bits 0-15) and log2 of the page size (bits 16 and up),
-// which place the chunk's list entries.
-template <int D, int G, bool PAGED, bool SPARSE, bool QK_MFMA>
+// is the first list the chunk reads (the chosen pages, the page scores when
+// the kernel selects the pages itself, else the page table, else unused) and
+// `list_width` its row width; `chunk_geom` packs the key tiles per chunk
+// (bits 0-15) and log2 of the page size (bits 16 and up), which place the
+// chunk's list entries.
+//
+// SEL_R > 0 (selected-page stream only): every workgroup of a unit runs the
+// top-K over the unit's page scores itself (select_top_k, SEL_R scores per
+// thread) and keeps the part of the ascending choice that its chunk covers;
+// the first split also writes the choice out.  All workgroups of a unit make
+// the same integer decisions on the same scores, so this equals a separate
+// top-K launch followed by the selected-page attention, with one launch less.
+template <int D, int G, bool PAGED, bool SPARSE, bool QK_MFMA, int SEL_R>
 __global__ void __launch_bounds__(kThreads)
     decode_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
-                  void* v, const int32_t* __restrict__ list, int batch, int hkv, int list_width,
+                  void* v, const void* __restrict__ list, int batch, int hkv, int list_width,
                   int chunk_geom, AttnLaunch a) {
+  constexpr bool SELECT = SEL_R > 0;
+  static_assert(!SELECT || SPARSE, "page selection feeds the selected-page stream");
+  static_assert(!SELECT || kThreads == kTopkThreads, "one workgroup shape for both parts");
   constexpr int NCK = Layout<D>::NCK;
   constexpr int NCV = Layout<D>::NCV;
   constexpr int NV = Layout<D>::NV;
@@ -278,11 +290,24 @@ __global__ void __launch_bounds__(kThreads)
   // wait.  (The page table of a dense paged stream is left to the compiler,
   // which issues it after the wait: early loads there measured 2% slower on
   // the var-length batch, where half of the workgroups have no keys.)
-  constexpr int kListIters = (PAGED || SPARSE) ? (kMaxChunkPages + kThreads - 1) / kThreads : 0;
+  constexpr int kListIters =
+      ((PAGED || SPARSE) && !SELECT) ? (kMaxChunkPages + kThreads - 1) / kThreads : 0;
   int raw_logical[kListIters > 0 ? kListIters : 1];
   int raw_phys[kListIters > 0 ? kListIters : 1];
   const int32_t* list_row =
-      (PAGED || SPARSE) ? list + (SPARSE ? unit : (int64_t)b) * list_width : nullptr;
+      kListIters > 0
+          ? reinterpret_cast<const int32_t*>(list) + (SPARSE ? unit : (int64_t)b) * list_width
+          : nullptr;
+  // Page scores of the unit (selecting mode), all loaded up front at indices
+  // clamped to the row; entries past the valid pages are masked in the
+  // selection.
+  float sel_raw[SELECT ? SEL_R : 1];
+  if constexpr (SELECT) {
+    const float* srow = reinterpret_cast<const float*>(list) + unit * list_width;
+#pragma unroll
+    for (int r = 0; r < SEL_R; ++r)
+      sel_raw[r] = early_load(srow + min(r * kThreads + (int)threadIdx.x, list_width - 1));
+  }
 #pragma unroll
   for (int r = 0; r < kListIters; ++r) {
     const int e = min(page0 + (int)threadIdx.x + r * kThreads, list_width - 1);
@@ -293,7 +318,7 @@ __global__ void __launch_bounds__(kThreads)
       if constexpr (PAGED) raw_phys[r] = list_row[e];
     }
   }
-  if constexpr (PAGED && SPARSE) {
+  if constexpr (PAGED && SPARSE && !SELECT) {
 #pragma unroll
     for (int r = 0; r < kListIters; ++r)
       raw_phys[r] = a.page_table[(int64_t)b * a.max_pages + min(max(raw_logical[r], 0), a.max_pages - 1)];
@@ -309,6 +334,11 @@ __global__ void __launch_bounds__(kThreads)
   if (split >= nsplit) {
     if (split == 0) {  // no valid key at all: defined as a zero output
       for (int i = threadIdx.x; i < G * D; i += kThreads) out[i] = (f16)0.0f;
+      if constexpr (SELECT) {  // and no page to choose
+        if (a.sel_idx_out != nullptr)
+          for (int i = threadIdx.x; i < a.num_sel; i += kThreads)
+            a.sel_idx_out[unit * a.num_sel + i] = -1;
+      }
     }
     return;
   }
@@ -320,7 +350,37 @@ __global__ void __launch_bounds__(kThreads)
   // Page lists of this chunk into LDS: the physical page of each logical page
   // (paged cache) and/or the chosen logical pages (selected-page stream).
   // Entries that do not name an existing page become -1.
-  if constexpr (PAGED || SPARSE) {
+  if constexpr (SELECT) {
+    // The unit's choice, of which this chunk keeps positions [page0, page0 +
+    // npg); the first split writes all of it out.
+    const int npg = (key_last >> shift) - page0 + 1;
+    const int K = a.num_sel;
+    const int n_scored = min(n_pages_L, list_width);
+    int32_t* idx_out =
+        (split == 0 && a.sel_idx_out != nullptr) ? a.sel_idx_out + unit * K : nullptr;
+    auto emit = [&](int pos, int page) {
+      if (idx_out != nullptr) idx_out[pos] = page;
+      const int li = pos - page0;
+      if (li >= 0 && li < npg) s_page[li] = page;
+    };
+    if (n_scored <= K) {
+      choose_all(n_scored, K, emit);
+    } else {
+      select_top_k<SEL_R>(sel_raw, n_scored, K, emit);
+    }
+    __syncthreads();
+    if constexpr (PAGED) {
+      for (int i = threadIdx.x; i < npg; i += kThreads) {
+        const int logical = s_page[i];
+        int phys = (logical >= 0 && logical < a.max_pages)
+                       ? a.page_table[(int64_t)b * a.max_pages + logical]
+                       : -1;
+        if (phys < 0 || phys >= a.num_pages) phys = -1;
+        s_phys[i] = phys;
+      }
+      __syncthreads();
+    }
+  } else if constexpr (PAGED || SPARSE) {
     const int npg = (key_last >> shift) - page0 + 1;
 #pragma unroll
     for (int r = 0; r < kListIters; ++r) {
@@ -627,19 +687,21 @@ __global__ void __launch_bounds__(G * D)
                               [&] { return stream_info(a, seqlens, b, SPARSE).nsplit; });
 }
 
-template <int D, int G, bool PAGED, bool SPARSE>
+template <int D, int G, bool PAGED, bool SPARSE, int SEL_R>
 int launch_one(const AttnLaunch& a, hipStream_t stream) {
-  const int32_t* list = SPARSE ? a.page_idx : a.page_table;
-  const int list_width = SPARSE ? a.num_sel : (PAGED ? a.max_pages : 1);
+  const void* list = SEL_R > 0 ? static_cast<const void*>(a.sel_scores)
+                   : SPARSE    ? static_cast<const void*>(a.page_idx)
+                               : static_cast<const void*>(a.page_table);
+  const int list_width = SEL_R > 0 ? a.sel_row : SPARSE ? a.num_sel : (PAGED ? a.max_pages : 1);
   // tiles per chunk < 2^16 (at most kMaxTilesPerSplitContiguous)
   const int chunk_geom = a.tiles_per_split | (a.page_shift << 16);
   const dim3 grid((uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads);
-  if (a.qk_mfma) {
-    hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, true>), grid, dim3(kThreads), 0,
+  if (a.qk_mfma || SEL_R > 0) {  // the selecting variant is built with q.k on the MFMA only
+    hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, true, SEL_R>), grid, dim3(kThreads), 0,
                        stream, a.seqlens, a.q, a.k, a.v, list, a.batch, a.num_kv_heads,
                        list_width, chunk_geom, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, false>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, false, 0>), grid, dim3(kThreads), 0,
                        stream, a.seqlens, a.q, a.k, a.v, list, a.batch, a.num_kv_heads,
                        list_width, chunk_geom, a);
   }
@@ -650,13 +712,26 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
+// Items per thread of the in-kernel top-K: the score row in 256-thread blocks.
+template <int D, int G, bool PAGED>
+int launch_select(const AttnLaunch& a, hipStream_t s) {
+  const int P = a.sel_row;
+  if (P <= kTopkThreads * 8) return launch_one<D, G, PAGED, true, 8>(a, s);
+  if (P <= kTopkThreads * 16) return launch_one<D, G, PAGED, true, 16>(a, s);
+  if (P <= kTopkThreads * 32) return launch_one<D, G, PAGED, true, 32>(a, s);
+  if (P <= kTopkThreads * 64) return launch_one<D, G, PAGED, true, 64>(a, s);
+  return (int)hipErrorInvalidValue;
+}
+
 template <int D, int G>
 int launch_dg(const AttnLaunch& a, hipStream_t s) {
   const bool paged = a.page_table != nullptr;
+  if (a.sel_scores != nullptr)
+    return paged ? launch_select<D, G, true>(a, s) : launch_select<D, G, false>(a, s);
   const bool sparse = a.page_idx != nullptr;
   if (paged)
-    return sparse ? launch_one<D, G, true, true>(a, s) : launch_one<D, G, true, false>(a, s);
-  return sparse ? launch_one<D, G, false, true>(a, s) : launch_one<D, G, false, false>(a, s);
+    return sparse ? launch_one<D, G, true, true, 0>(a, s) : launch_one<D, G, true, false, 0>(a, s);
+  return sparse ? launch_one<D, G, false, true, 0>(a, s) : launch_one<D, G, false, false, 0>(a, s);
 }
 
 template <int D>

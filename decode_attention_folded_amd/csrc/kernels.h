@@ -36,6 +36,12 @@ struct AttnLaunch {
   int32_t tiles_per_split;   // key tiles per workgroup chunk
   int32_t max_splits;        // splits per (b, kv) unit; the grid is max_splits * B * Hkv
   float scale_log2;          // scale * log2(e)
+  // Pages chosen in the launch (sel_scores != nullptr, page_idx == nullptr):
+  // every workgroup runs the top-K of its unit's page scores and attends over
+  // its part of the choice; split 0 writes the choice to sel_idx_out.
+  const float* sel_scores;   // [B, Hkv, sel_row] page scores, or nullptr
+  int32_t* sel_idx_out;      // [B, Hkv, num_sel] or nullptr
+  int32_t sel_row;           // score row width (<= 16384)
   int32_t qk_mfma;           // 1: q.k on the matrix cores, 0: v_dot2 on the VALU
 };
 

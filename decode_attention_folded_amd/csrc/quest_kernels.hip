@@ -34,6 +34,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace da {
 namespace {
@@ -257,51 +258,14 @@ __global__ void __launch_bounds__(kWave * kScoreWaves)
 
 // ------------------------------------------------------------ top-K
 
-constexpr int kTopkThreads = 256;
-constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kRadixBits = 11;
-constexpr int kMaxRankCand = 64;  // boundary candidates resolved by exact ranking
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  // Larger float -> larger key; -0 is folded into +0 first.
-  const uint32_t u = __builtin_bit_cast(uint32_t, f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// One workgroup per (b, kv).  Thread t holds items i = k * 256 + t (k < R):
-// coalesced loads, and the selected set is kept as an LDS bitmap whose words
-// are written with wave ballots (word of item i = i / 32).
-//   1. keys = order-preserving u32 of the scores; skip the bits shared by the
-//      smallest and largest key;
-//   2. radix passes on 11-bit digits: LDS histogram of the remaining
-//      candidates, boundary digit by a digit-descending block scan; items
-//      above it are taken, below it dropped;
-//   3. once at most 64 candidates tie on the boundary, each is ranked exactly
-//      by (key descending, index ascending); if all 32 key bits are used up
-//      with more candidates, the lowest indices win;
-//   4. the bitmap is compacted in index order (ascending output, -1 pad).
-//
+// One workgroup per (b, kv): select_top_k over the unit's score row.
 // Leading scalar arguments as in the score kernel: the score row and its
 // width, so the score loads issue together with the valid-length load.
 template <int R>
 __global__ void __launch_bounds__(kTopkThreads)
     topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ seqlens, int hkv,
                 int row_pages, ScoreLaunch a) {
-  static_assert(R >= 8 && R <= 64 && R % 8 == 0, "items per thread");
-  constexpr int NW = R * kTopkThreads / 32;                      // bitmap words
-  constexpr int WPT = (NW + kTopkThreads - 1) / kTopkThreads;    // words per thread
-  __shared__ uint32_t hist[1 << kRadixBits];
-  __shared__ uint32_t info[3];
-  __shared__ uint32_t scratch[kTopkWaves];
-  __shared__ uint32_t red_min[kTopkWaves], red_max[kTopkWaves];
-  __shared__ uint32_t selbits[NW];
-  __shared__ uint32_t candbits[NW];
-  __shared__ uint32_t ckey[kMaxRankCand];
-  __shared__ int32_t cidx[kMaxRankCand];
-
   const int tid = threadIdx.x;
-  const int lane = lane_in_wave();
-  const int wave = tid / kWave;
   const int kv = blockIdx.x;
   const int b = blockIdx.y;
   const int64_t unit = (int64_t)b * hkv + kv;
@@ -309,7 +273,7 @@ __global__ void __launch_bounds__(kTopkThreads)
   // The length and all score loads first, unconditionally, the scores at
   // indices clamped to the row (not to the valid pages, which wait for the
   // length), so they are in flight together; entries past the valid pages are
-  // masked below.  Early loads are not moved past the exit below.
+  // masked in the selection.  Early loads are not moved past the exit below.
   int L = early_load(seqlens + b);
   float raw[R];
 #pragma unroll
@@ -320,207 +284,12 @@ __global__ void __launch_bounds__(kTopkThreads)
   L = L < 0 ? 0 : L;
   int n_pages = (L + (1 << a.page_shift) - 1) >> a.page_shift;
   if (n_pages > row_pages) n_pages = row_pages;
-  if (n_pages <= K) {  // every existing page is chosen
-    for (int i = tid; i < K; i += kTopkThreads) dst[i] = i < n_pages ? i : -1;
+  auto emit = [&](int pos, int page) { dst[pos] = page; };
+  if (n_pages <= K) {
+    choose_all(n_pages, K, emit);
     return;
   }
-
-  uint32_t key[R];
-  uint64_t cand = 0;   // bit k: item k is still a candidate
-  uint64_t take = 0;   // bit k: item k is chosen
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    const bool valid = k * kTopkThreads + tid < n_pages;
-    const uint32_t kk = order_key(raw[k]);
-    key[k] = valid ? kk : 0u;
-    cand |= (uint64_t)valid << k;
-    kmin = min(kmin, valid ? kk : 0xFFFFFFFFu);
-    kmax = max(kmax, valid ? kk : 0u);
-  }
-  kmin = wave_min(kmin);
-  kmax = wave_max(kmax);
-  if (lane == 0) {
-    red_min[wave] = kmin;
-    red_max[wave] = kmax;
-  }
-  __syncthreads();
-  kmin = red_min[0];
-  kmax = red_max[0];
-#pragma unroll
-  for (int w = 1; w < kTopkWaves; ++w) {
-    kmin = min(kmin, red_min[w]);
-    kmax = max(kmax, red_max[w]);
-  }
-  const uint32_t diff = kmin ^ kmax;
-  int shift = diff ? 32 - __builtin_clz(diff) : 0;  // bits below the common prefix
-  uint32_t need = (uint32_t)K;
-  uint32_t ncand = (uint32_t)n_pages;
-
-  while (need > 0 && need < ncand && shift > 0 && ncand > (uint32_t)kMaxRankCand) {
-    const int nb = shift < kRadixBits ? shift : kRadixBits;
-    shift -= nb;
-    const uint32_t nbins = 1u << nb;
-    for (uint32_t i = tid; i < nbins; i += kTopkThreads) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const bool c = (cand >> k) & 1;
-      if (__ballot(c) != 0)  // wave-uniform: skip slots with no candidate
-        atomicAdd(&hist[(key[k] >> shift) & (nbins - 1)], c ? 1u : 0u);
-    }
-    __syncthreads();
-    // thread t sums a run of `per` digits taken from the top digit down
-    const int per = (int)((nbins + kTopkThreads - 1) / kTopkThreads);
-    uint32_t run = 0;
-    for (int q = 0; q < per; ++q) {
-      const int dgt = (int)nbins - 1 - (tid * per + q);
-      if (dgt >= 0) run += hist[dgt];
-    }
-    uint32_t total;
-    const uint32_t before = block_exclusive_scan<kTopkWaves>(run, scratch, &total);
-    if (before < need && need <= before + run) {
-      uint32_t acc = before;
-      for (int q = 0; q < per; ++q) {
-        const int dgt = (int)nbins - 1 - (tid * per + q);
-        if (dgt < 0) break;
-        const uint32_t cnt = hist[dgt];
-        if (acc + cnt >= need) {
-          info[0] = (uint32_t)dgt;  // boundary digit
-          info[1] = acc;            // candidates above it
-          info[2] = cnt;            // candidates on it
-          break;
-        }
-        acc += cnt;
-      }
-    }
-    __syncthreads();
-    const uint32_t dstar = info[0];
-    const uint32_t above = info[1];
-    const uint32_t on = info[2];
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const uint32_t dg = (key[k] >> shift) & (nbins - 1);
-      const uint64_t bit = (uint64_t)1 << k;
-      if (dg > dstar) take |= cand & bit;
-      if (dg != dstar) cand &= ~bit;
-    }
-    need -= above;
-    ncand = on;
-    __syncthreads();  // hist and info are reused by the next pass
-  }
-  if (need >= ncand) {  // the remaining candidates all fit
-    take |= cand;
-    cand = 0;
-  }
-
-  // chosen items -> bitmap (each (slot, wave) owns two words)
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    const uint64_t m = __ballot((take >> k) & 1);
-    if (lane == 0) {
-      selbits[k * 8 + 2 * wave] = (uint32_t)m;
-      selbits[k * 8 + 2 * wave + 1] = (uint32_t)(m >> 32);
-    }
-  }
-  __syncthreads();
-
-  if (need > 0 && need < ncand) {
-    if (ncand <= (uint32_t)kMaxRankCand) {
-      // exact ranking of the boundary candidates by (key desc, index asc):
-      // list them in LDS, each thread at the block prefix of its candidate
-      // count (plain stores; an LDS atomic per slot costs a round trip each),
-      // then rank each one
-      uint32_t listed_total;
-      uint32_t pos = block_exclusive_scan<kTopkWaves>((uint32_t)__builtin_popcountll(cand),
-                                                      scratch, &listed_total);
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        if ((cand >> k) & 1) {  // ncand <= 64 candidates exist: pos < 64
-          ckey[pos] = key[k];
-          cidx[pos] = k * kTopkThreads + tid;
-          ++pos;
-        }
-      }
-      __syncthreads();
-      // four threads per candidate (a quad), each comparing it with a
-      // quarter of the list; the quad's counts add up through DPP
-      constexpr int kPerPart = kMaxRankCand / 4;
-      const int c = tid >> 2;
-      const int part = tid & 3;
-      const bool has = c < (int)ncand;
-      const uint32_t kc = has ? ckey[c] : 0u;
-      const int ic = has ? cidx[c] : 0x7FFFFFFF;
-      uint32_t rank = 0;
-#pragma unroll
-      for (int u = 0; u < kPerPart; ++u) {
-        const int j = part + 4 * u;
-        const uint32_t kj = ckey[j];
-        const int ij = cidx[j];
-        rank += (j < (int)ncand) && ((kj > kc) || (kj == kc && ij < ic));
-      }
-      rank += dpp_u32<kDppXor1, 0xF, 0xF>(rank);
-      rank += dpp_u32<kDppXor2, 0xF, 0xF>(rank);
-      if (has && part == 0 && rank < need) atomicOr(&selbits[ic >> 5], 1u << (ic & 31));
-    } else {
-      // all key bits used and more equal keys than places: lowest indices win
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const uint64_t cb = __ballot((cand >> k) & 1);
-        if (lane == 0) {
-          candbits[k * 8 + 2 * wave] = (uint32_t)cb;
-          candbits[k * 8 + 2 * wave + 1] = (uint32_t)(cb >> 32);
-        }
-      }
-      __syncthreads();
-      uint32_t mine = 0;
-#pragma unroll
-      for (int q = 0; q < WPT; ++q) {
-        const int w = tid * WPT + q;
-        if (w < NW) mine += __builtin_popcount(candbits[w]);
-      }
-      uint32_t total;
-      uint32_t rank = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
-#pragma unroll
-      for (int q = 0; q < WPT; ++q) {
-        const int w = tid * WPT + q;
-        if (w >= NW) break;
-        uint32_t bits = candbits[w];
-        uint32_t keep = 0;
-        while (bits != 0 && rank < need) {
-          const uint32_t low = bits & (~bits + 1u);
-          keep |= low;
-          bits ^= low;
-          ++rank;
-        }
-        if (keep) atomicOr(&selbits[w], keep);
-      }
-    }
-    __syncthreads();
-  }
-
-  // ascending compaction of the bitmap
-  uint32_t mine = 0;
-#pragma unroll
-  for (int q = 0; q < WPT; ++q) {
-    const int w = tid * WPT + q;
-    if (w < NW) mine += __builtin_popcount(selbits[w]);
-  }
-  uint32_t total;
-  uint32_t pos = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
-#pragma unroll
-  for (int q = 0; q < WPT; ++q) {
-    const int w = tid * WPT + q;
-    if (w >= NW) break;
-    uint32_t bits = selbits[w];
-    while (bits != 0) {
-      const int bit = __builtin_ctz(bits);
-      bits &= bits - 1;
-      if (pos < (uint32_t)K) dst[pos] = w * 32 + bit;
-      ++pos;
-    }
-  }
-  for (uint32_t i = total + tid; i < (uint32_t)K; i += kTopkThreads) dst[i] = -1;
+  select_top_k<R>(raw, n_pages, K, emit);
 }
 
 template <int D, int G>
@@ -579,7 +348,7 @@ int launch_score_topk(const ScoreLaunch& in, void* stream) {
   int err = a.head_dim == 64 ? launch_score_d<64>(a, s)
           : a.head_dim == 128 ? launch_score_d<128>(a, s)
                               : (int)hipErrorInvalidValue;
-  if (err != 0) return err;
+  if (err != 0 || a.page_idx == nullptr) return err;  // scores only
   const int P = a.meta_max_pages;
   if (P <= kTopkThreads * 8) return launch_topk<8>(a, s);
   if (P <= kTopkThreads * 16) return launch_topk<16>(a, s);

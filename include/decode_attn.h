@@ -209,6 +209,8 @@ int da_quest_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t meta_ma
  *              from token budget"); must be a positive multiple of S.
  *   page_idx   (device) int32 [B, Hkv, K] out: the min(K, P_b) chosen pages in
  *              ascending page order, then -1.  Ties in U go to the lower index.
+ *              NULL: scores only (no top-K launch); page_scores is then
+ *              required, e.g. for quest_select_sparse_decode_attn.
  *   page_scores (device) fp32 [B, Hkv, meta_max_pages] out, or NULL to keep the
  *              scores in the workspace.  Entries p >= P_b are not written.
  *   workspace  (device) >= da_quest_workspace_size(...) bytes when
@@ -242,7 +244,8 @@ int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_page
  *              L_b = 0 appends nothing)
  *   k_new, v_new (device) fp16 [B, Hkv, D], both required
  *   budget_tokens, page_idx, page_scores, workspace: as quest_page_score_topk
- *   (the workspace size is da_quest_workspace_size(B, Hkv, meta_max_pages)).
+ *   (the workspace size is da_quest_workspace_size(B, Hkv, meta_max_pages);
+ *   page_idx NULL with page_scores given: the append and the scores only).
  */
 int quest_append_score_topk(const void* q, const da_kv_cache* kv, void* meta,
                             int32_t meta_max_pages, const int32_t* seqlens, int32_t num_q_heads,
@@ -267,6 +270,37 @@ int quest_sparse_decode_attn(const void* q, const da_kv_cache* kv, const int32_t
                              const int32_t* page_idx, int32_t budget_tokens,
                              int32_t num_q_heads, float scale, void* out, void* workspace,
                              size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/*
+ * Top-K page selection fused into the attention over the chosen pages: the
+ * effect of the top-K half of quest_page_score_topk followed by
+ * quest_sparse_decode_attn, with bit-identical choice and output, in one
+ * attention launch (plus the split merge) instead of two.  [Quest-review]
+ * (paper section 3.4 and the flowchart of section 3.3): keep the K pages
+ * with the highest score, then attend over their tokens only.  Every
+ * workgroup of a (b, kv) unit selects from the unit's scores itself and
+ * attends over its share of the choice.
+ *
+ *   page_scores (device) fp32 [B, Hkv, meta_max_pages] as written by
+ *              quest_page_score_topk or quest_append_score_topk (with page_idx
+ *              NULL, for the scores alone); entries p >= P_b are ignored.
+ *   meta_max_pages  row width of page_scores; meta_max_pages * S >= the
+ *              per-sequence capacity; <= 16384
+ *   page_idx   (device) int32 [B, Hkv, K] out: the choice, as
+ *              quest_page_score_topk writes it; or NULL
+ *   budget_tokens, q, kv, seqlens, num_q_heads, scale, out, workspace
+ *              (da_workspace_size(kv, Hq, budget_tokens, num_splits) bytes),
+ *              num_splits, stream: as quest_sparse_decode_attn.
+ * Returns DA_ERR_NULL if page_scores is NULL (B > 0), DA_ERR_SHAPE if
+ * meta_max_pages does not cover the capacity, DA_ERR_UNSUPPORTED above 16384
+ * pages, otherwise as quest_sparse_decode_attn.
+ */
+int quest_select_sparse_decode_attn(const void* q, const da_kv_cache* kv,
+                                    const int32_t* seqlens, const float* page_scores,
+                                    int32_t meta_max_pages, int32_t budget_tokens,
+                                    int32_t num_q_heads, float scale, int32_t* page_idx,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    int32_t num_splits, void* stream);
 
 /*
  * Measurement helper, not part of the method: the HBM read rate a plain

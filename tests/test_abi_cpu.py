@@ -76,6 +76,30 @@ def test_read_calibration_validation_codes(lib):
     assert lib.da_read_calibration(P(FAKE + 8), 1 << 20, P(FAKE), None) == -2
 
 
+def test_select_sparse_validation_codes(lib):
+    P = ctypes.c_void_p
+
+    def call(desc=None, scores=FAKE, meta_pages=256, budget=256, hq=32, idx=None, out=FAKE,
+             ws_bytes=1 << 30):
+        desc = desc if desc is not None else _desc()
+        return lib.quest_select_sparse_decode_attn(P(FAKE), ctypes.byref(desc), P(FAKE),
+                                                   P(scores) if scores else None, meta_pages,
+                                                   budget, hq, 0.125, P(idx) if idx else None,
+                                                   P(out) if out else None, P(FAKE), ws_bytes, 0,
+                                                   None)
+    assert call(scores=0) == -1                                # page scores required
+    assert call(out=0) == -1
+    assert call(budget=100) == -4                              # not a multiple of S
+    assert call(budget=0) == -4
+    assert call(meta_pages=255) == -2                          # 255 * 16 < capacity 4096
+    assert call(meta_pages=0) == -2
+    assert call(desc=_desc(capacity=1 << 20), meta_pages=1 << 16) == -3   # > 16384 pages
+    assert call(desc=_desc(page_size=12)) == -3
+    assert call(hq=30) == -2
+    assert call(ws_bytes=16) == -5
+    assert call(desc=_desc(batch=0), scores=0, out=0) == 0     # nothing to do
+
+
 def test_status_strings(lib):
     for code in range(0, -7, -1):
         s = lib.da_status_string(code).decode()
