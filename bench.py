@@ -424,7 +424,8 @@ def kernel_source_digest():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_folded_amd", "csrc")
-    for name in ("decode_kernel.hip", "quest_kernels.hip", "device_common.h", "kernels.h"):
+    for name in ("attention_impl.h", "decode_kernel.hip", "decode_select.hip", "topk.h",
+                 "quest_kernels.hip", "device_common.h", "kernels.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

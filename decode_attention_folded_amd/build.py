@@ -5,6 +5,7 @@ compiles the HIP kernels and the C ABI layer into
 ``decode_attention_folded_amd/libdecode_attn.so``.  Always rebuilds.
 """
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -16,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libdecode_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-HIP_SOURCES = ["decode_kernel.hip", "quest_kernels.hip", "repeat_kv.hip", "calibrate.hip"]
+HIP_SOURCES = ["decode_kernel.hip", "decode_select.hip", "quest_kernels.hip", "repeat_kv.hip",
+               "calibrate.hip"]
 HOST_SOURCES = ["api.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code.  The kernels'
@@ -54,16 +56,20 @@ def build(verbose=True, out_dir=None):
     hipcc = _hipcc()
     out_dir = out_dir or os.path.join(PKG, "_build")
     os.makedirs(out_dir, exist_ok=True)
-    objs = []
+    jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(out_dir, src + ".o")
-        _run([hipcc, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([hipcc, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
     for src in HOST_SOURCES:
         obj = os.path.join(out_dir, src + ".o")
-        _run([hipcc, "-O2", "-std=c++17", "-fPIC", "-Wall", "-x", "c++", "-c",
-              os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([hipcc, "-O2", "-std=c++17", "-fPIC", "-Wall", "-x", "c++", "-c",
+                      os.path.join(CSRC, src), "-o", obj], obj))
+    # the translation units compile independently: run them side by side
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd, _ in jobs]:
+            f.result()
+    objs = [obj for _, obj in jobs]
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)

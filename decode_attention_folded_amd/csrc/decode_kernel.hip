@@ -1,733 +1,15 @@
-// Split-context folded-GQA decode attention for gfx950 (MI355X).
-//
-// What it computes -- [CoreML-GQA] section 3, "Fold Q Instead of Expanding KV"
-// and "Implementation": for every (batch b, KV head kv) the G query heads
-// h = G*kv + g are treated as G rows of one small matrix, so each K and V row
-// is read from HBM once for all G rows (no repeat_kv copy).  Per row:
-// s_t = scale * q.k_t for t < L_b, softmax over t, o = sum_t p_t v_t.
-// With q_len > 1 query positions per head ([CoreML-GQA] section 5, "Prefill
-// Needs Separate Design") the rows are the G * q_len (head, position) pairs of
-// the KV head -- group and sequence axes merged -- and row g * q_len + i only
-// sees keys t < L_b - q_len + 1 + i.  The template parameter G is the row
-// count.  The Quest variant ([Quest-review], paper sections 3.3-3.5) runs the
-// same loop over the tokens of the chosen pages only.
-//
-// Work decomposition (flash-decode): a 1-D grid of splits x (B * Hkv) units,
-// unit index fastest.  A workgroup of 4 waves owns a contiguous chunk of
-// `tiles_per_split` 16-key tiles of one (b, kv) unit; its waves take the
-// chunk's tiles round robin.  Workgroups reach the 8 XCDs round robin, so with
-// the unit index fastest every XCD receives the same KV heads of every
-// sequence: sequences of different lengths load the XCDs evenly, which they
-// do not when the split index runs fastest (short sequences would only feed
-// the XCDs of the low split numbers).
-// Each split writes a partial (running max m, sum l, unnormalised o) and a
-// second, small launch merges them (log-sum-exp, in split order).  The kernel
-// boundary is the only synchronisation: merging inside the attention kernel
-// needs either device-scope release/acquire fences (which write back /
-// invalidate the whole L2 of every XCD and cost a third of the runtime) or a
-// hand-off through agent-scope (write-through) stores, an arrival counter and
-// agent-scope loads, which measured no faster than the extra launch on small
-// grids and about 5% slower on large ones (every workgroup must wait for its
-// write-through stores before it retires).
-//
-// Lane layout of one 16-key tile (lane = 0..63):
-//   K: lane holds key (lane % 16), 16-byte channel chunks 4*j + lane/16,
-//      j < D/32 -- the B-operand layout of v_mfma_f32_16x16x16f16 (k =
-//      channel, n = key), so a tile feeds the matrix core as loaded.
-//   V: lane holds keys (lane % 8) and (lane % 8) + 8, chunks 8*h + lane/8,
-//      h < D/64: each load instruction covers 128 contiguous bytes of each
-//      of 8 keys, and a lane accumulates only D/8 channels per query row.
-// Scores: with QK_MFMA the G query rows are replicated over the 16 rows of
-// the MFMA A operand, so every lane receives all G scores of its K key; the
-// VALU variant (v_dot2_f32_f16 over the lane's channels, then a sum over the
-// 4 lanes of the key) gives the same placement.  One DPP exchange (lane ^ 8)
-// hands each lane the scores of its two V keys.
-// Each lane keeps its own online-softmax state (m, l, fp32 accumulators) over
-// the keys that pass through its slots; the 8 slot states of a channel group
-// are merged at the end of the chunk, then the 4 waves through LDS.
-// Rescaling is lazy: the running max only moves when a score exceeds it by
-// more than 2^8 (exp2 units), so steady-state tiles skip the rescale.
-// Tiles are loaded into a ring of NS register stages, so NS - 1 tiles are in
-// flight while one is computed.
-//
-// Keys at or past the valid length are never loaded from their own slots:
-// their loads are redirected to a valid row of the same sequence and their
-// scores forced to -inf, so whatever the cache holds there (even NaN) cannot
-// leak into the result.  No floating-point atomics: results are bitwise
-// reproducible.
+// Folded-GQA decode attention (attention_impl.h): the instantiations for a
+// contiguous or paged cache, dense or over a given list of chosen pages, and
+// the launch entry used by the C ABI.
 
-#include <hip/hip_runtime.h>
-#include <math.h>
-#include <stdint.h>
-
-#include "device_common.h"
-#include "kernels.h"
-#include "topk.h"
+#include "attention_impl.h"
 
 namespace da {
 namespace {
 
-typedef f16 f16x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = 4;
-constexpr int kThreads = kWave * kWaves;
-constexpr int kTileKeys = 16;
-// Key tiles per workgroup chunk, at most: 128 when the chunk reads a page
-// list (paged cache or chosen pages; the list is staged in LDS), 256 for a
-// contiguous cache.  Measured on MI355X: contiguous 128K dense attention
-// 672 us at 128, 642 at 256, 635 at 512; the variable-length paged batch 706,
-// 715 and 761 us (coarser chunks leave a longer tail of unequal sequences).
-constexpr int kMaxTilesPerSplit = 128;
-constexpr int kMaxTilesPerSplitContiguous = 256;
-constexpr int kMinPageSize = 8;
-// pages (or chosen-page entries) one chunk can touch
-constexpr int kMaxChunkPages = kMaxTilesPerSplit * kTileKeys / kMinPageSize + 2;
-constexpr float kRescaleThreshold = 8.0f;
-constexpr float kNegBig = -1.0e30f;
-constexpr int kStages = 3;
-
-// Keys in the (b, kv) key stream and the number of splits that cover it;
-// shared by the attention and the merge kernel.
-struct StreamInfo {
-  int L;        // valid length after clamping
-  int n_keys;   // keys in the stream (dense: L; chosen pages: nsel * S)
-  int nsplit;   // splits with at least one key
-};
-
-__device__ __forceinline__ StreamInfo stream_info(const AttnLaunch& a, const int32_t* seqlens, int b,
-                                                  bool sparse) {
-  StreamInfo si;
-  const int L = seqlens[b];
-  si.L = L < 0 ? 0 : (L > a.capacity ? a.capacity : L);
-  si.n_keys = si.L;
-  if (sparse) {
-    const int pages = (si.L + (1 << a.page_shift) - 1) >> a.page_shift;
-    const int nsel = pages < a.num_sel ? pages : a.num_sel;
-    si.n_keys = nsel << a.page_shift;
-  }
-  const int n_tiles = (si.n_keys + kTileKeys - 1) / kTileKeys;
-  si.nsplit = (n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;
-  return si;
-}
-
-template <int D>
-struct Layout {
-  static constexpr int NCK = D / 32;   // K chunks per lane per tile
-  static constexpr int NCV = D / 64;   // V chunks per lane per key (2 keys)
-  static constexpr int NV = NCV * 8;   // channels per lane
-};
-
-template <int D>
-struct Stage {
-  f16x8 k[Layout<D>::NCK];
-  f16x8 v0[Layout<D>::NCV];  // key (lane % 8)
-  f16x8 v1[Layout<D>::NCV];  // key (lane % 8) + 8
-  bool kvalid;               // the K key of this lane
-  int ktok;                  // its token position (causal limit of q_len > 1 rows)
-};
-
-// Merge the split partials of one unit into its G output rows:
-// O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the splits, in split
-// order (log-sum-exp).  Every thread merges whole output elements on its own,
-// reading each split's (m, l) itself, so the loads of a batch issue together;
-// the first batch is read before `get_nsplit` is called (it may wait for the
-// valid length).  Splits past the valid ones are dropped by selects, so stale
-// workspace contents never enter the sums.
-template <int D, int G, int NT, typename NSplitFn>
-__device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float* part_ml,
-                                               const float* part_o, int max_splits, int64_t unit,
-                                               NSplitFn get_nsplit) {
-  constexpr int kIters = (G * D + NT - 1) / NT;  // output elements per thread
-  constexpr int kBatch = 32 / kIters;            // splits per load batch
-  const float2* ml = reinterpret_cast<const float2*>(part_ml) + unit * max_splits * G;
-  const float* po = part_o + unit * max_splits * G * D;
-  f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;
-
-  float M[kIters], O[kIters], S[kIters];
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    M[it] = kNegBig;
-    O[it] = 0.0f;
-    S[it] = 0.0f;
-  }
-  float2 mv[kIters][kBatch];
-  float ov[kIters][kBatch];
-  auto load_batch = [&](int s0, auto load) {
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int i = min((int)threadIdx.x + it * NT, G * D - 1);
-      const int g = i / D;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int sp = min(s0 + u, max_splits - 1);
-        mv[it][u] = load(ml + sp * G + g);
-        ov[it][u] = load(po + (int64_t)sp * G * D + i);
-      }
-    }
-  };
-  auto add_batch = [&](int s0, int nsplit) {
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      float bm = M[it];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) bm = s0 + u < nsplit ? fmaxf(bm, mv[it][u].x) : bm;
-      const float f = fast_exp2(M[it] - bm);
-      float o = O[it] * f, l = S[it] * f;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float w = s0 + u < nsplit ? fast_exp2(mv[it][u].x - bm) : 0.0f;
-        o = fmaf(w, s0 + u < nsplit ? ov[it][u] : 0.0f, o);
-        l = fmaf(w, s0 + u < nsplit ? mv[it][u].y : 0.0f, l);
-      }
-      M[it] = bm;
-      O[it] = o;
-      S[it] = l;
-    }
-  };
-  // The first batch is issued before anything else (its addresses need only
-  // the leading arguments, and early loads are not moved past the exit
-  // below); later batches follow one by one.
-  load_batch(0, [](const auto* p) { return early_load(p); });
-  const int nsplit = get_nsplit();
-  if (nsplit <= 1) return;  // the attention kernel wrote the output
-  add_batch(0, nsplit);
-  for (int s0 = kBatch; s0 < nsplit; s0 += kBatch) {
-    load_batch(s0, [](const auto* p) { return *p; });
-    add_batch(s0, nsplit);
-  }
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int i = (int)threadIdx.x + it * NT;
-    if (i < G * D) out[i] = (f16)(S[it] > 0.0f ? O[it] / S[it] : 0.0f);
-  }
-}
-
-// The leading scalar arguments repeat the fields of `a` that the first
-// instructions need (see `launch_one`); the rest of `a` is read from the
-// kernel-argument segment while the valid-length load is in flight.  `list`
-// is the first list the chunk reads (the chosen pages, the page scores when
-// the kernel selects the pages itself, else the page table, else unused) and
-// `list_width` its row width; `chunk_geom` packs the key tiles per chunk
-// (bits 0-15) and log2 of the page size (bits 16 and up), which place the
-// chunk's list entries.
-//
-// SEL_R > 0 (selected-page stream only): every workgroup of a unit runs the
-// top-K over the unit's page scores itself (select_top_k, SEL_R scores per
-// thread) and keeps the part of the ascending choice that its chunk covers;
-// the first split also writes the choice out.  All workgroups of a unit make
-// the same integer decisions on the same scores, so this equals a separate
-// top-K launch followed by the selected-page attention, with one launch less.
-template <int D, int G, bool PAGED, bool SPARSE, bool QK_MFMA, int SEL_R>
-__global__ void __launch_bounds__(kThreads)
-    decode_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
-                  void* v, const void* __restrict__ list, int batch, int hkv, int list_width,
-                  int chunk_geom, AttnLaunch a) {
-  constexpr bool SELECT = SEL_R > 0;
-  static_assert(!SELECT || SPARSE, "page selection feeds the selected-page stream");
-  static_assert(!SELECT || kThreads == kTopkThreads, "one workgroup shape for both parts");
-  constexpr int NCK = Layout<D>::NCK;
-  constexpr int NCV = Layout<D>::NCV;
-  constexpr int NV = Layout<D>::NV;
-  constexpr int GC = (G + 3) / 4;  // MFMA chains (4 query rows each)
-  constexpr int NS = kStages;
-
-  __shared__ float s_o[kWaves][G][D];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-  __shared__ int32_t s_page[(PAGED || SPARSE) ? kMaxChunkPages : 1];
-  __shared__ int32_t s_phys[(PAGED && SPARSE) ? kMaxChunkPages : 1];
-
-  const int lane = lane_in_wave();
-  const int wave = threadIdx.x / kWave;
-  const int rk = lane & 15;        // K key slot
-  const int ck = lane >> 4;        // K chunk group (0..3)
-  const int rv = lane & 7;         // V key slots rv, rv + 8
-  const int cv = lane >> 3;        // V chunk group (0..7)
-  const bool upper = (lane & 8) != 0;
-  // grid < 2^31 workgroups (checked on the host): 32-bit index arithmetic
-  const uint32_t n_units = (uint32_t)batch * (uint32_t)hkv;
-  const uint32_t split_u = blockIdx.x / n_units;
-  const uint32_t unit_u = blockIdx.x - split_u * n_units;
-  const uint32_t b_u = unit_u / (uint32_t)hkv;
-  const int split = (int)split_u;
-  const int64_t unit = unit_u;
-  const int b = (int)b_u;
-  const int kv = (int)(unit_u - b_u * (uint32_t)hkv);
-  const int tiles_per_split = chunk_geom & 0xFFFF;
-  const int shift = chunk_geom >> 16;
-  const int page_mask = (1 << shift) - 1;
-  const int tile_begin = split * tiles_per_split;
-  const int key_begin = tile_begin * kTileKeys;
-  const int page0 = key_begin >> shift;
-
-  // Inputs that do not depend on the valid length: the folded queries and the
-  // raw page-list entries of the whole chunk (clamped indices; checked once
-  // the length is known).
-  const f16* qb = reinterpret_cast<const f16*>(q) + unit * G * D;
-  // MFMA A operand: row i of chain c is query g = (4c + i % 4) mod G; the lane
-  // holds row lane % 16 over the k-slots of chunk 4j + ck.
-  f16x8 qa[QK_MFMA ? GC : 1][QK_MFMA ? NCK : 1];
-  // VALU operand: all G rows over the lane's K channels.
-  f16x8 qv[QK_MFMA ? 1 : G][QK_MFMA ? 1 : NCK];
-  if constexpr (QK_MFMA) {
-#pragma unroll
-    for (int cch = 0; cch < GC; ++cch) {
-      const int g = (4 * cch + (rk & 3)) % G;
-#pragma unroll
-      for (int j = 0; j < NCK; ++j)
-        qa[cch][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < NCK; ++j)
-        qv[g][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
-  }
-  // Entry i of the chunk's page list: the chosen logical page (selected-page
-  // stream) and/or the physical page (paged cache), read with clamped indices.
-  // The chosen pages are read with early loads, ahead of the valid-length
-  // wait.  (The page table of a dense paged stream is left to the compiler,
-  // which issues it after the wait: early loads there measured 2% slower on
-  // the var-length batch, where half of the workgroups have no keys.)
-  constexpr int kListIters =
-      ((PAGED || SPARSE) && !SELECT) ? (kMaxChunkPages + kThreads - 1) / kThreads : 0;
-  int raw_logical[kListIters > 0 ? kListIters : 1];
-  int raw_phys[kListIters > 0 ? kListIters : 1];
-  const int32_t* list_row =
-      kListIters > 0
-          ? reinterpret_cast<const int32_t*>(list) + (SPARSE ? unit : (int64_t)b) * list_width
-          : nullptr;
-  // Page scores of the unit (selecting mode), all loaded up front at indices
-  // clamped to the row; entries past the valid pages are masked in the
-  // selection.
-  float sel_raw[SELECT ? SEL_R : 1];
-  if constexpr (SELECT) {
-    const float* srow = reinterpret_cast<const float*>(list) + unit * list_width;
-#pragma unroll
-    for (int r = 0; r < SEL_R; ++r)
-      sel_raw[r] = early_load(srow + min(r * kThreads + (int)threadIdx.x, list_width - 1));
-  }
-#pragma unroll
-  for (int r = 0; r < kListIters; ++r) {
-    const int e = min(page0 + (int)threadIdx.x + r * kThreads, list_width - 1);
-    if constexpr (SPARSE) {
-      raw_logical[r] = early_load(list_row + e);
-    } else {
-      raw_logical[r] = page0 + (int)threadIdx.x + r * kThreads;
-      if constexpr (PAGED) raw_phys[r] = list_row[e];
-    }
-  }
-  if constexpr (PAGED && SPARSE && !SELECT) {
-#pragma unroll
-    for (int r = 0; r < kListIters; ++r)
-      raw_phys[r] = a.page_table[(int64_t)b * a.max_pages + min(max(raw_logical[r], 0), a.max_pages - 1)];
-  }
-
-  const StreamInfo si = stream_info(a, seqlens, b, SPARSE);
-  const int L = si.L;
-  const int n_keys = si.n_keys;
-  const int nsplit = si.nsplit;
-  const int n_pages_L = (L + page_mask) >> shift;
-  f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;  // rows h = G*kv + g of batch b
-
-  if (split >= nsplit) {
-    if (split == 0) {  // no valid key at all: defined as a zero output
-      for (int i = threadIdx.x; i < G * D; i += kThreads) out[i] = (f16)0.0f;
-      if constexpr (SELECT) {  // and no page to choose
-        if (a.sel_idx_out != nullptr)
-          for (int i = threadIdx.x; i < a.num_sel; i += kThreads)
-            a.sel_idx_out[unit * a.num_sel + i] = -1;
-      }
-    }
-    return;
-  }
-
-  const int n_tiles = (n_keys + kTileKeys - 1) / kTileKeys;
-  const int tile_end = min(tile_begin + tiles_per_split, n_tiles);
-  const int key_last = min(tile_end * kTileKeys, n_keys) - 1;
-
-  // Page lists of this chunk into LDS: the physical page of each logical page
-  // (paged cache) and/or the chosen logical pages (selected-page stream).
-  // Entries that do not name an existing page become -1.
-  if constexpr (SELECT) {
-    // The unit's choice, of which this chunk keeps positions [page0, page0 +
-    // npg); the first split writes all of it out.
-    const int npg = (key_last >> shift) - page0 + 1;
-    const int K = a.num_sel;
-    const int n_scored = min(n_pages_L, list_width);
-    int32_t* idx_out =
-        (split == 0 && a.sel_idx_out != nullptr) ? a.sel_idx_out + unit * K : nullptr;
-    auto emit = [&](int pos, int page) {
-      if (idx_out != nullptr) idx_out[pos] = page;
-      const int li = pos - page0;
-      if (li >= 0 && li < npg) s_page[li] = page;
-    };
-    if (n_scored <= K) {
-      choose_all(n_scored, K, emit);
-    } else {
-      select_top_k<SEL_R>(sel_raw, n_scored, K, emit);
-    }
-    __syncthreads();
-    if constexpr (PAGED) {
-      for (int i = threadIdx.x; i < npg; i += kThreads) {
-        const int logical = s_page[i];
-        int phys = (logical >= 0 && logical < a.max_pages)
-                       ? a.page_table[(int64_t)b * a.max_pages + logical]
-                       : -1;
-        if (phys < 0 || phys >= a.num_pages) phys = -1;
-        s_phys[i] = phys;
-      }
-      __syncthreads();
-    }
-  } else if constexpr (PAGED || SPARSE) {
-    const int npg = (key_last >> shift) - page0 + 1;
-#pragma unroll
-    for (int r = 0; r < kListIters; ++r) {
-      const int i = (int)threadIdx.x + r * kThreads;
-      if (i < npg) {
-        int logical = raw_logical[r];
-        if constexpr (SPARSE) {
-          if (logical < 0 || logical >= n_pages_L) logical = -1;
-        }
-        int entry = logical;
-        if constexpr (PAGED) {
-          int phys = raw_phys[r];
-          if (logical < 0 || logical >= a.max_pages || phys < 0 || phys >= a.num_pages) phys = -1;
-          if constexpr (SPARSE) {
-            s_phys[i] = phys;
-          } else {
-            entry = phys;
-          }
-        }
-        s_page[i] = entry;
-      }
-    }
-    __syncthreads();
-  }
-
-  // Masked keys load a row that holds this sequence's data (token 0, valid
-  // because L >= 1 here) instead of their own slot, so the value multiplied by
-  // their zero weight is finite.  A page-table entry outside the pool falls
-  // back to pool page 0, which always exists.
-  int64_t safe_off;
-  if constexpr (PAGED) {
-    int phys0 = a.page_table[(int64_t)b * a.max_pages];
-    if (phys0 < 0 || phys0 >= a.num_pages) phys0 = 0;
-    safe_off = (((int64_t)phys0 * hkv + kv) << shift) * D;
-  } else {
-    safe_off = unit * a.cache_stride * D;
-  }
-
-  const f16* kc = reinterpret_cast<const f16*>(k);
-  const f16* vc = reinterpret_cast<const f16*>(v);
-  const bool has_new = a.k_new != nullptr;
-  const f16* knew_row = has_new ? reinterpret_cast<const f16*>(a.k_new) + unit * D : nullptr;
-  const f16* vnew_row = has_new ? reinterpret_cast<const f16*>(a.v_new) + unit * D : nullptr;
-
-  // Row r of the unit is query position r % q_len of head G * kv + r / q_len
-  // (group and sequence axes merged); it sees keys t < L - q_len + 1 + r % q_len.
-  // With q_len = 1 every row sees the whole valid length.
-  int lim[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) lim[g] = L - a.q_len + 1 + g % a.q_len;
-
-  float m[G], l[G], acc[G][NV];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegBig;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int x = 0; x < NV; ++x) acc[g][x] = 0.0f;
-  }
-
-  // Append: the new row goes to slot L - 1 of the cache.  Only the workgroup
-  // whose chunk holds that slot writes it, and its own loads of that key are
-  // redirected to k_new/v_new, so no other read of the slot can race.
-  if (has_new && !SPARSE && key_begin <= L - 1 && L - 1 <= key_last) {
-    int64_t off;
-    if constexpr (PAGED) {
-      int phys = a.page_table[(int64_t)b * a.max_pages + ((L - 1) >> shift)];
-      off = (phys >= 0 && phys < a.num_pages)
-                ? (((int64_t)phys * hkv + kv) << shift) * D + (int64_t)((L - 1) & page_mask) * D
-                : -1;
-    } else {
-      off = (unit * a.cache_stride + (L - 1)) * D;
-    }
-    if (off >= 0 && threadIdx.x < 2 * (D / 8)) {
-      const int c16 = threadIdx.x % (D / 8);
-      const f16* src = (threadIdx.x < D / 8 ? knew_row : vnew_row) + 8 * c16;
-      f16* dst = reinterpret_cast<f16*>(threadIdx.x < D / 8 ? k : v) + off + 8 * c16;
-      *reinterpret_cast<f16x8*>(dst) = *reinterpret_cast<const f16x8*>(src);
-    }
-  }
-
-  // Element offset of stream position j (or the safe row), its validity and
-  // its token index.  Positions outside this chunk (live = false) resolve to
-  // the safe row: the stage ring issues its loads unconditionally so that the
-  // compiler's wait counts stay exact, and such loads only touch that row.
-  auto resolve = [&](int j, bool live, bool& valid, int& t) -> int64_t {
-    t = j;
-    valid = live && j < n_keys;
-    int64_t off;
-    // The list entries are read unconditionally (the index is in range
-    // either way) and masked afterwards, so the reads of a stage issue
-    // together instead of each behind a branch and a wait.
-    if constexpr (SPARSE) {
-      const int li = valid ? (j >> shift) - page0 : 0;  // in range of the LDS list
-      const int logical_raw = s_page[li];
-      const int phys_raw = PAGED ? s_phys[li] : 0;
-      const int logical = valid ? logical_raw : -1;
-      t = (logical << shift) + (j & page_mask);
-      valid = valid && logical >= 0 && t < L;
-      if constexpr (PAGED) {
-        const int phys = valid ? phys_raw : -1;
-        valid = valid && phys >= 0;
-        off = (((int64_t)phys * hkv + kv) << shift) * D + (int64_t)(t & page_mask) * D;
-      } else {
-        off = (unit * a.cache_stride + t) * D;
-      }
-    } else if constexpr (PAGED) {
-      const int phys_raw = s_page[valid ? (j >> shift) - page0 : 0];
-      const int phys = valid ? phys_raw : -1;
-      valid = valid && phys >= 0;
-      off = (((int64_t)phys * hkv + kv) << shift) * D + (int64_t)(t & page_mask) * D;
-    } else {
-      off = (unit * a.cache_stride + t) * D;
-    }
-    return valid ? off : safe_off;
-  };
-
-  // Loads of one tile; no branches, so every stage issues the same number of
-  // loads and the wait for a stage leaves the later stages in flight.
-  auto load_stage = [&](int tile, Stage<D>& st) {
-    const bool live = tile < tile_end;
-    const int j0 = tile * kTileKeys;
-    bool vk, v0, v1;
-    int tk, t0, t1;
-    const int64_t ok = resolve(j0 + rk, live, vk, tk);
-    const int64_t o0 = resolve(j0 + rv, live, v0, t0);
-    const int64_t o1 = resolve(j0 + rv + 8, live, v1, t1);
-    st.kvalid = vk;
-    st.ktok = tk;
-    // The appended key reads k_new/v_new; with an append, masked keys read it
-    // too (the slot being written may not hold finite data yet).
-    const f16* kp = (has_new && (!vk || tk == L - 1)) ? knew_row : kc + ok;
-    const f16* vp0 = (has_new && (!v0 || t0 == L - 1)) ? vnew_row : vc + o0;
-    const f16* vp1 = (has_new && (!v1 || t1 == L - 1)) ? vnew_row : vc + o1;
-    // K and V are streamed once: non-temporal loads (measured about 20%
-    // more read bandwidth than default-policy loads on this part).
-#pragma unroll
-    for (int j = 0; j < NCK; ++j)
-      st.k[j] = stream_load(kp + 8 * (4 * j + ck));
-#pragma unroll
-    for (int h = 0; h < NCV; ++h) {
-      st.v0[h] = stream_load(vp0 + 8 * (8 * h + cv));
-      st.v1[h] = stream_load(vp1 + 8 * (8 * h + cv));
-    }
-  };
-
-  auto compute_stage = [&](const Stage<D>& st) {
-    // scores of this lane's K key, all G rows
-    float sk[G];
-    if constexpr (QK_MFMA) {
-#pragma unroll
-      for (int cch = 0; cch < GC; ++cch) {
-        f32x4 d4 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int j = 0; j < NCK; ++j) {
-          const f16x4 blo = {st.k[j][0], st.k[j][1], st.k[j][2], st.k[j][3]};
-          const f16x4 bhi = {st.k[j][4], st.k[j][5], st.k[j][6], st.k[j][7]};
-          const f16x4 alo = {qa[cch][j][0], qa[cch][j][1], qa[cch][j][2], qa[cch][j][3]};
-          const f16x4 ahi = {qa[cch][j][4], qa[cch][j][5], qa[cch][j][6], qa[cch][j][7]};
-          d4 = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, d4, 0, 0, 0);
-          d4 = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, d4, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * cch + r < G) sk[4 * cch + r] = d4[r];
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float x = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NCK; ++j) x = dot8(qv[g][j], st.k[j], x);
-        x += lane_xor<16>(x);
-        x += lane_xor<32>(x);
-        sk[g] = x;
-      }
-    }
-    // scores of the two V keys of this lane: keys (lane % 8) and + 8
-    float sa[G], sb[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mine = (st.kvalid && st.ktok < lim[g]) ? sk[g] * a.scale_log2 : -INFINITY;
-      const float other = lane_xor<8>(mine);
-      sa[g] = upper ? other : mine;
-      sb[g] = upper ? mine : other;
-    }
-    bool need = false;
-#pragma unroll
-    for (int g = 0; g < G; ++g) need |= fmaxf(sa[g], sb[g]) > m[g] + kRescaleThreshold;
-    if (need) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float mn = fmaxf(m[g], fmaxf(sa[g], sb[g]));
-        const float f = fast_exp2(m[g] - mn);
-        l[g] *= f;
-#pragma unroll
-        for (int x = 0; x < NV; ++x) acc[g][x] *= f;
-        m[g] = mn;
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float pa = fast_exp2(sa[g] - m[g]);
-      const float pb = fast_exp2(sb[g] - m[g]);
-      l[g] += pa + pb;
-#pragma unroll
-      for (int h = 0; h < NCV; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = fmaf(pa, (float)st.v0[h][e], acc[g][h * 8 + e]);
-          acc[g][h * 8 + e] = fmaf(pb, (float)st.v1[h][e], x);
-        }
-    }
-  };
-
-  // Ring of NS register stages: stage s holds the wave's tiles first + s*4,
-  // first + (s + NS)*4, ... (4 = waves per workgroup, the wave's stride).
-  {
-    Stage<D> st[NS];
-    const int first = tile_begin + wave;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) load_stage(first + s * kWaves, st[s]);
-    for (int base = first; base < tile_end; base += NS * kWaves) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int t = base + s * kWaves;
-        if (t < tile_end) compute_stage(st[s]);
-        load_stage(t + NS * kWaves, st[s]);
-      }
-    }
-  }
-
-  // Merge the 8 key slots of each V channel group (log-sum-exp).
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float M = group_max<8>(m[g]);
-    const float f = fast_exp2(m[g] - M);
-    l[g] = group_sum<8>(l[g] * f);
-#pragma unroll
-    for (int x = 0; x < NV; ++x) acc[g][x] = group_sum<8>(acc[g][x] * f);
-    m[g] = M;
-  }
-  if (rv == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int h = 0; h < NCV; ++h) {
-        float* dst = &s_o[wave][g][8 * (8 * h + cv)];
-        *reinterpret_cast<f32x4*>(dst) =
-            f32x4{acc[g][h * 8 + 0], acc[g][h * 8 + 1], acc[g][h * 8 + 2], acc[g][h * 8 + 3]};
-        *reinterpret_cast<f32x4*>(dst + 4) =
-            f32x4{acc[g][h * 8 + 4], acc[g][h * 8 + 5], acc[g][h * 8 + 6], acc[g][h * 8 + 7]};
-      }
-      if (cv == 0) {
-        s_m[wave][g] = m[g];
-        s_l[wave][g] = l[g];
-      }
-    }
-  }
-  __syncthreads();
-
-  // Merge the waves of this workgroup; write the output (single split) or
-  // this split's partial.
-  float* part_o = a.part_o + (unit * a.max_splits + split) * G * D;
-  float* part_ml = a.part_ml + (unit * a.max_splits + split) * G * 2;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int g = i / D;
-    const int d = i % D;
-    float M = s_m[0][g];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
-    float o = 0.0f, lsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(s_m[w][g] - M);
-      o += f * s_o[w][g][d];
-      lsum += f * s_l[w][g];
-    }
-    if (nsplit == 1) {
-      out[i] = (f16)(lsum > 0.0f ? o / lsum : 0.0f);
-    } else {
-      part_o[i] = o;
-      if (d == 0) {
-        part_ml[2 * g] = M;
-        part_ml[2 * g + 1] = lsum;
-      }
-    }
-  }
-}
-
-// Merge kernel: one workgroup per (b, kv) unit, one thread per output element
-// of the unit's G rows (G * D threads, 64 to 1024), so every thread merges a
-// batch of up to 32 splits with one round of loads.
-// Leading scalar arguments as in the attention kernel: what the first batch
-// of partial loads needs.
-template <int D, int G, bool SPARSE>
-__global__ void __launch_bounds__(G * D)
-    merge_kernel(const float* __restrict__ part_ml, const float* __restrict__ part_o,
-                 const int32_t* __restrict__ seqlens, int max_splits, int hkv, AttnLaunch a) {
-  const int kv = blockIdx.x;
-  const int b = blockIdx.y;
-  const int64_t unit = (int64_t)b * hkv + kv;
-  merge_partials<D, G, G * D>(a, part_ml, part_o, max_splits, unit,
-                              [&] { return stream_info(a, seqlens, b, SPARSE).nsplit; });
-}
-
-template <int D, int G, bool PAGED, bool SPARSE, int SEL_R>
-int launch_one(const AttnLaunch& a, hipStream_t stream) {
-  const void* list = SEL_R > 0 ? static_cast<const void*>(a.sel_scores)
-                   : SPARSE    ? static_cast<const void*>(a.page_idx)
-                               : static_cast<const void*>(a.page_table);
-  const int list_width = SEL_R > 0 ? a.sel_row : SPARSE ? a.num_sel : (PAGED ? a.max_pages : 1);
-  // tiles per chunk < 2^16 (at most kMaxTilesPerSplitContiguous)
-  const int chunk_geom = a.tiles_per_split | (a.page_shift << 16);
-  const dim3 grid((uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads);
-  if (a.qk_mfma || SEL_R > 0) {  // the selecting variant is built with q.k on the MFMA only
-    hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, true, SEL_R>), grid, dim3(kThreads), 0,
-                       stream, a.seqlens, a.q, a.k, a.v, list, a.batch, a.num_kv_heads,
-                       list_width, chunk_geom, a);
-  } else {
-    hipLaunchKernelGGL((decode_kernel<D, G, PAGED, SPARSE, false, 0>), grid, dim3(kThreads), 0,
-                       stream, a.seqlens, a.q, a.k, a.v, list, a.batch, a.num_kv_heads,
-                       list_width, chunk_geom, a);
-  }
-  const int err = (int)hipGetLastError();
-  if (err != 0 || a.max_splits <= 1) return err;
-  hipLaunchKernelGGL((merge_kernel<D, G, SPARSE>), dim3(a.num_kv_heads, a.batch), dim3(G * D), 0,
-                     stream, a.part_ml, a.part_o, a.seqlens, a.max_splits, a.num_kv_heads, a);
-  return (int)hipGetLastError();
-}
-
-// Items per thread of the in-kernel top-K: the score row in 256-thread blocks.
-template <int D, int G, bool PAGED>
-int launch_select(const AttnLaunch& a, hipStream_t s) {
-  const int P = a.sel_row;
-  if (P <= kTopkThreads * 8) return launch_one<D, G, PAGED, true, 8>(a, s);
-  if (P <= kTopkThreads * 16) return launch_one<D, G, PAGED, true, 16>(a, s);
-  if (P <= kTopkThreads * 32) return launch_one<D, G, PAGED, true, 32>(a, s);
-  if (P <= kTopkThreads * 64) return launch_one<D, G, PAGED, true, 64>(a, s);
-  return (int)hipErrorInvalidValue;
-}
-
 template <int D, int G>
 int launch_dg(const AttnLaunch& a, hipStream_t s) {
   const bool paged = a.page_table != nullptr;
-  if (a.sel_scores != nullptr)
-    return paged ? launch_select<D, G, true>(a, s) : launch_select<D, G, false>(a, s);
   const bool sparse = a.page_idx != nullptr;
   if (paged)
     return sparse ? launch_one<D, G, true, true, 0>(a, s) : launch_one<D, G, true, false, 0>(a, s);
@@ -754,6 +36,7 @@ int max_tiles_per_split(bool page_list) {
 }
 
 int launch_decode(const AttnLaunch& a, void* stream) {
+  if (a.sel_scores != nullptr) return launch_select_attention(a, stream);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (a.head_dim == 64) return launch_d<64>(a, s);
   if (a.head_dim == 128) return launch_d<128>(a, s);

@@ -56,6 +56,8 @@ int keys_per_tile(int head_dim, int group);
 int max_tiles_per_split(bool page_list);  // page_list: paged cache or chosen pages
 
 int launch_decode(const AttnLaunch& p, void* stream);
+// the selecting variant (p.sel_scores != nullptr); called by launch_decode
+int launch_select_attention(const AttnLaunch& p, void* stream);
 
 struct MetaLaunch {
   void* k;                   // cache or pool (written only when k_new != nullptr)
