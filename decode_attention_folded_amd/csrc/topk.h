@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace da {
@@ -57,19 +59,21 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
   __shared__ uint32_t ckey[kMaxRankCand];
   __shared__ int32_t cidx[kMaxRankCand];
 
+  // one bit per item of the thread: 32-bit masks while they suffice
+  using Mask = typename std::conditional<(R <= 32), uint32_t, uint64_t>::type;
   const int tid = threadIdx.x;
   const int lane = lane_in_wave();
   const int wave = tid / kWave;
   uint32_t key[R];
-  uint64_t cand = 0;   // bit k: item k is still a candidate
-  uint64_t take = 0;   // bit k: item k is chosen
+  Mask cand = 0;   // bit k: item k is still a candidate
+  Mask take = 0;   // bit k: item k is chosen
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const bool valid = k * kTopkThreads + tid < n_pages;
     const uint32_t kk = order_key(raw[k]);
     key[k] = valid ? kk : 0u;
-    cand |= (uint64_t)valid << k;
+    cand |= (Mask)valid << k;
     kmin = min(kmin, valid ? kk : 0xFFFFFFFFu);
     kmax = max(kmax, valid ? kk : 0u);
   }
@@ -79,6 +83,8 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
     red_min[wave] = kmin;
     red_max[wave] = kmax;
   }
+  // the first pass's histogram is cleared under the same barrier
+  for (int i = tid; i < (1 << kRadixBits); i += kTopkThreads) hist[i] = 0u;
   __syncthreads();
   kmin = red_min[0];
   kmax = red_max[0];
@@ -96,8 +102,6 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
     const int nb = shift < kRadixBits ? shift : kRadixBits;
     shift -= nb;
     const uint32_t nbins = 1u << nb;
-    for (uint32_t i = tid; i < nbins; i += kTopkThreads) hist[i] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const bool c = (cand >> k) & 1;
@@ -105,28 +109,32 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
         atomicAdd(&hist[(key[k] >> shift) & (nbins - 1)], c ? 1u : 0u);
     }
     __syncthreads();
-    // thread t sums a run of `per` digits taken from the top digit down
+    // thread t sums a run of `per` digits taken from the top digit down,
+    // keeping the counts in registers for the boundary search
+    constexpr int kPerMax = (1 << kRadixBits) / kTopkThreads;
     const int per = (int)((nbins + kTopkThreads - 1) / kTopkThreads);
+    uint32_t cnt[kPerMax];
     uint32_t run = 0;
-    for (int q = 0; q < per; ++q) {
+#pragma unroll
+    for (int q = 0; q < kPerMax; ++q) {
       const int dgt = (int)nbins - 1 - (tid * per + q);
-      if (dgt >= 0) run += hist[dgt];
+      cnt[q] = (q < per && dgt >= 0) ? hist[dgt] : 0u;
+      run += cnt[q];
     }
     uint32_t total;
     const uint32_t before = block_exclusive_scan<kTopkWaves>(run, scratch, &total);
     if (before < need && need <= before + run) {
       uint32_t acc = before;
-      for (int q = 0; q < per; ++q) {
-        const int dgt = (int)nbins - 1 - (tid * per + q);
-        if (dgt < 0) break;
-        const uint32_t cnt = hist[dgt];
-        if (acc + cnt >= need) {
-          info[0] = (uint32_t)dgt;  // boundary digit
-          info[1] = acc;            // candidates above it
-          info[2] = cnt;            // candidates on it
-          break;
+      bool found = false;
+#pragma unroll
+      for (int q = 0; q < kPerMax; ++q) {
+        if (!found && acc + cnt[q] >= need) {
+          info[0] = (uint32_t)((int)nbins - 1 - (tid * per + q));  // boundary digit
+          info[1] = acc;                                           // candidates above it
+          info[2] = cnt[q];                                        // candidates on it
+          found = true;
         }
-        acc += cnt;
+        acc += cnt[q];
       }
     }
     __syncthreads();
@@ -136,12 +144,14 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const uint32_t dg = (key[k] >> shift) & (nbins - 1);
-      const uint64_t bit = (uint64_t)1 << k;
+      const Mask bit = (Mask)1 << k;
       if (dg > dstar) take |= cand & bit;
       if (dg != dstar) cand &= ~bit;
     }
     need -= above;
     ncand = on;
+    // the next pass's histogram (nobody reads this one any more)
+    for (int i = tid; i < (int)nbins; i += kTopkThreads) hist[i] = 0u;
     __syncthreads();  // hist and info are reused by the next pass
   }
   if (need >= ncand) {  // the remaining candidates all fit
