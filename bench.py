@@ -651,12 +651,15 @@ def quest_sweep(da, torch, seed, dev, steps, warmup, flush):
             kp = budget // S
             idx = torch.empty((b, h, kp), dtype=torch.int32, device=dev)
             scores = torch.empty((b, h, P), dtype=torch.float32, device=dev)
+            # the Quest step as launched by default: scores, then the top-K
+            # fused into the selected-page attention
             fns = [lambda: da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=S,
-                                                    budget_tokens=budget, page_idx=idx,
-                                                    page_scores=scores),
-                   lambda: da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx,
-                                                       budget_tokens=budget, page_size=S,
-                                                       out=out, workspace=ws)]
+                                                    budget_tokens=budget, page_scores=scores,
+                                                    select=False),
+                   lambda: da.quest_select_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"],
+                                                              scores, budget_tokens=budget,
+                                                              page_size=S, page_idx=idx,
+                                                              out=out, workspace=ws)]
             for f in fns:
                 f()
             torch.cuda.synchronize()
@@ -695,6 +698,7 @@ def quest_sweep(da, torch, seed, dev, steps, warmup, flush):
             da.quest_meta_append(cl["k"], cl["v"], cl["meta"], cl["seqlens"], n_new=L,
                                  page_size=16)
             cl["idx"] = torch.empty((b, h, 128), dtype=torch.int32, device=dev)
+            cl["scores"] = torch.empty((b, h, L // 16), dtype=torch.float32, device=dev)
         layers.append(cl)
 
     def dense_layer(cl):
@@ -702,10 +706,10 @@ def quest_sweep(da, torch, seed, dev, steps, warmup, flush):
 
     def quest_layer(cl):
         da.quest_page_score_topk(cl["q"], cl["meta"], cl["seqlens"], page_size=16,
-                                 budget_tokens=2048, page_idx=cl["idx"])
-        da.quest_sparse_decode_attn(cl["q"], cl["k"], cl["v"], cl["seqlens"], cl["idx"],
-                                    budget_tokens=2048, page_size=16, out=cl["out"],
-                                    workspace=ws)
+                                 budget_tokens=2048, page_scores=cl["scores"], select=False)
+        da.quest_select_sparse_decode_attn(cl["q"], cl["k"], cl["v"], cl["seqlens"], cl["scores"],
+                                           budget_tokens=2048, page_size=16, page_idx=cl["idx"],
+                                           out=cl["out"], workspace=ws)
 
     all_dense = [lambda cl=cl: dense_layer(cl) for cl in layers]
     policy = [lambda cl=cl, l=l: dense_layer(cl) if l < 2 else quest_layer(cl)

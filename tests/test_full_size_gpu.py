@@ -125,12 +125,21 @@ def test_full_quest_llama2_32k(da):
     P = L // s
     meta = torch.zeros((b, hkv, P, 2, d), dtype=torch.float16, device=DEV)
     da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], n_new=L, page_size=s)
+    # the step as bench.py runs it: scores, then the top-K fused into the
+    # selected-page attention
     scores = torch.empty((b, hkv, P), dtype=torch.float32, device=DEV)
-    idx = da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s, budget_tokens=budget,
-                                   page_scores=scores)
-    out = da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx,
-                                      budget_tokens=budget, page_size=s)
+    da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s, budget_tokens=budget,
+                             page_scores=scores, select=False)
+    idx = torch.empty((b, hkv, budget // s), dtype=torch.int32, device=DEV)
+    out = da.quest_select_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], scores,
+                                             budget_tokens=budget, page_size=s, page_idx=idx)
+    # with the top-K as its own launch: the same choice and output, bit for bit
+    idx2 = da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s,
+                                    budget_tokens=budget)
+    out2 = da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx2,
+                                       budget_tokens=budget, page_size=s)
     torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(out, out2)
     got = f64(out)
     assert np.all(np.isfinite(got))
     meta_h, scores_h, idx_h = host(meta), host(scores), host(idx)
@@ -149,8 +158,9 @@ def test_full_quest_gqa_128k_step(da):
     """The long-context Quest GQA step: B=8, Hq=32, Hkv=8, D=128, L=131072,
     S=16, budget 4096 (K=256), 16 planted pages per unit.  Metadata is built
     in bulk, then the step appends one K/V row at slot 131071 with its
-    metadata update inside the score launch (quest_append_score_topk), scores
-    and selects pages, and attends over them; dense
+    metadata update inside the score launch (quest_append_score_topk, scores
+    only), then selects pages and attends over them in one launch
+    (quest_select_sparse_decode_attn); dense
     attention at the same shape (64 splits per unit) runs beside it.
     Sampled units are checked against the oracle run through the same steps."""
     b, hq, hkv, d, L, s, budget = 8, 32, 8, 128, 131072, 16, 4096
@@ -164,15 +174,24 @@ def test_full_quest_gqa_128k_step(da):
     torch.cuda.synchronize()
     k_before = {u: host(c["k"][u[0]:u[0] + 1, u[1]:u[1] + 1]) for u in units}
     v_before = {u: host(c["v"][u[0]:u[0] + 1, u[1]:u[1] + 1]) for u in units}
-    # the step, as bench.py runs it: append fused into the score launch
+    # the step, as bench.py runs it: the append fused into the score launch,
+    # then the top-K fused into the selected-page attention
     scores = torch.empty((b, hkv, P), dtype=torch.float32, device=DEV)
-    idx = da.quest_append_score_topk(c["q"], c["k"], c["v"], meta, c["seqlens"], c["k_new"],
-                                     c["v_new"], page_size=s, budget_tokens=budget,
-                                     page_scores=scores)
-    out = da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx,
-                                      budget_tokens=budget, page_size=s)
+    da.quest_append_score_topk(c["q"], c["k"], c["v"], meta, c["seqlens"], c["k_new"],
+                               c["v_new"], page_size=s, budget_tokens=budget, page_scores=scores,
+                               select=False)
+    idx = torch.empty((b, hkv, budget // s), dtype=torch.int32, device=DEV)
+    out = da.quest_select_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], scores,
+                                             budget_tokens=budget, page_size=s, page_idx=idx)
     dense = da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"])
+    # on the appended cache and metadata, score + top-K then the attention over
+    # the given pages: the same choice and output, bit for bit
+    idx2 = da.quest_page_score_topk(c["q"], meta, c["seqlens"], page_size=s,
+                                    budget_tokens=budget)
+    out2 = da.quest_sparse_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], idx2,
+                                       budget_tokens=budget, page_size=s)
     torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(out, out2)
     got, got_dense = f64(out), f64(dense)
     assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_dense))
     meta_h, scores_h, idx_h = host(meta), host(scores), host(idx)
