@@ -431,11 +431,11 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload):
-    """HBM bytes per call of the dominant stage (its kernels summed) from the
-    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE runs,
-    scaled by a reference copy), or None if missing or taken on different
-    kernel sources."""
+def counter_traffic(workload, stage):
+    """HBM bytes per call of one stage (its kernels summed) from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a
+    reference copy), or None if missing or taken on different kernel
+    sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
     try:
         text = open(path).read()
@@ -446,7 +446,7 @@ def counter_traffic(workload):
     entry = data.get("workloads", {}).get(workload)
     if not entry or data.get("kernel_source_digest") != kernel_source_digest():
         return None
-    return entry.get("bytes_per_call")
+    return entry.get("stages", {}).get(stage, {}).get("bytes_per_call")
 
 
 def measure(torch, da, dev, step, steps, warmup, flush):
@@ -848,7 +848,7 @@ def main():
     torch.cuda.synchronize()
     del src, dst
 
-    traffic = counter_traffic(args.workload)
+    traffic = counter_traffic(args.workload, r["dominant"].name)
     cal = read_calibration(da, torch, dev, flush)
     line = {
         "metric": "decode-attn KV GB/s (% HBM peak) + us/step",
