@@ -134,78 +134,66 @@ struct Stage {
 
 // Merge the split partials of one unit into its G output rows:
 // O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the splits, in split
-// order (log-sum-exp).  Every thread merges whole output elements on its own,
-// reading each split's (m, l) itself, so the loads of a batch issue together;
-// the first batch is read before `get_nsplit` is called (it may wait for the
-// valid length).  Splits past the valid ones are dropped by selects, so stale
-// workspace contents never enter the sums.
+// order (log-sum-exp).  One thread per output element; D is a multiple of 64,
+// so every wave works on one row.  Lane s of a wave loads split s's (m, l) of
+// that row and the values reach the other lanes through readlane, so a round
+// of kBatch splits is 1 + kBatch loads per lane: within the 63 loads a wave
+// can keep in flight, so the round costs one memory round trip.  The first
+// round is read before `get_nsplit` is called (it may wait for the valid
+// length).  Splits past the valid ones get zero weight, so stale workspace
+// contents never enter the sums.
 template <int D, int G, int NT, typename NSplitFn>
 __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float* part_ml,
                                                const float* part_o, int max_splits, int64_t unit,
                                                NSplitFn get_nsplit) {
-  constexpr int kIters = (G * D + NT - 1) / NT;  // output elements per thread
-  constexpr int kBatch = 32 / kIters;            // splits per load batch
+  static_assert(NT == G * D && D % kWave == 0, "one thread per output element, one row per wave");
+  constexpr int kBatch = 48;  // splits per round of loads
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + unit * max_splits * G;
   const float* po = part_o + unit * max_splits * G * D;
   f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;
+  const int i = (int)threadIdx.x;  // output element
+  const int g = i / D;             // its row, the same for the whole wave
+  const int lane = lane_in_wave();
 
-  float M[kIters], O[kIters], S[kIters];
+  float M = kNegBig, O = 0.0f, S = 0.0f;
+  float2 mlv;          // (m, l) of split s0 + lane
+  float ov[kBatch];    // o of splits s0 .. s0 + kBatch - 1 at element i
+  auto load_round = [&](int s0, auto load) {
+    mlv = load(ml + min(s0 + lane, max_splits - 1) * G + g);
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    M[it] = kNegBig;
-    O[it] = 0.0f;
-    S[it] = 0.0f;
-  }
-  float2 mv[kIters][kBatch];
-  float ov[kIters][kBatch];
-  auto load_batch = [&](int s0, auto load) {
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int i = min((int)threadIdx.x + it * NT, G * D - 1);
-      const int g = i / D;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int sp = min(s0 + u, max_splits - 1);
-        mv[it][u] = load(ml + sp * G + g);
-        ov[it][u] = load(po + (int64_t)sp * G * D + i);
-      }
-    }
+    for (int u = 0; u < kBatch; ++u)
+      ov[u] = load(po + (int64_t)min(s0 + u, max_splits - 1) * G * D + i);
   };
-  auto add_batch = [&](int s0, int nsplit) {
+  auto add_round = [&](int s0, int nsplit) {
+    const bool mine = lane < kBatch && s0 + lane < nsplit;
+    const float m_s = mine ? mlv.x : kNegBig;
+    const float bm = fmaxf(M, wave_max_f32(m_s));
+    const float w_s = mine ? fast_exp2(m_s - bm) : 0.0f;
+    const float l_s = mine ? mlv.y : 0.0f;
+    const float f = fast_exp2(M - bm);
+    float o = O * f, l = S * f;
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      float bm = M[it];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) bm = s0 + u < nsplit ? fmaxf(bm, mv[it][u].x) : bm;
-      const float f = fast_exp2(M[it] - bm);
-      float o = O[it] * f, l = S[it] * f;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float w = s0 + u < nsplit ? fast_exp2(mv[it][u].x - bm) : 0.0f;
-        o = fmaf(w, s0 + u < nsplit ? ov[it][u] : 0.0f, o);
-        l = fmaf(w, s0 + u < nsplit ? mv[it][u].y : 0.0f, l);
-      }
-      M[it] = bm;
-      O[it] = o;
-      S[it] = l;
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = read_lane(w_s, u);
+      o = fmaf(w, s0 + u < nsplit ? ov[u] : 0.0f, o);
+      l = fmaf(w, read_lane(l_s, u), l);
     }
+    M = bm;
+    O = o;
+    S = l;
   };
-  // The first batch is issued before anything else (its addresses need only
+  // The first round is issued before anything else (its addresses need only
   // the leading arguments, and early loads are not moved past the exit
-  // below); later batches follow one by one.
-  load_batch(0, [](const auto* p) { return early_load(p); });
+  // below); later rounds follow one by one.
+  load_round(0, [](const auto* p) { return early_load(p); });
   const int nsplit = get_nsplit();
   if (nsplit <= 1) return;  // the attention kernel wrote the output
-  add_batch(0, nsplit);
+  add_round(0, nsplit);
   for (int s0 = kBatch; s0 < nsplit; s0 += kBatch) {
-    load_batch(s0, [](const auto* p) { return *p; });
-    add_batch(s0, nsplit);
+    load_round(s0, [](const auto* p) { return *p; });
+    add_round(s0, nsplit);
   }
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int i = (int)threadIdx.x + it * NT;
-    if (i < G * D) out[i] = (f16)(S[it] > 0.0f ? O[it] / S[it] : 0.0f);
-  }
+  out[i] = (f16)(S > 0.0f ? O / S : 0.0f);
 }
 
 // The leading scalar arguments repeat the fields of `a` that the first

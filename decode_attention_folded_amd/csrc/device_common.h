@@ -54,6 +54,18 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// Value of lane `l` (a wave-uniform index) as a scalar.
+__device__ __forceinline__ float read_lane(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// Maximum over the 64 lanes of a wave (wave-uniform result): the 16-lane
+// row maxima, then the four rows through readlane.
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = group_max<16>(x);
+  return fmaxf(fmaxf(read_lane(x, 0), read_lane(x, 16)), fmaxf(read_lane(x, 32), read_lane(x, 48)));
+}
+
 // Value of lane (lane ^ MASK) for MASK in {8, 16, 32}.
 template <int MASK>
 __device__ __forceinline__ float lane_xor(float x) {
