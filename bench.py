@@ -769,8 +769,8 @@ def read_calibration(da, torch, dev, flush, reps=10):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "no multi-GPU path exists", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "there is no multi-GPU path", file=sys.stderr)
         return 2
     import torch
     import decode_attention_folded_amd as da
