@@ -117,7 +117,9 @@ def exaone30(da, torch, seed, dev):
            "head_dim": d, "capacity": cap, "valid_len": L, "dtype_cache": "fp16"}
     st = Stage("attention", [lambda l=l: one(l) for l in range(layers)], layers * per_launch,
                "decode_kernel + merge_kernel (gqa_decode_attn)")
-    return Step("exaone30", cfg, layers * kv_layer, layers * per_launch, [st]), data
+    step = Step("exaone30", cfg, layers * kv_layer, layers * per_launch, [st])
+    step.kernels_per_step = 2 * layers  # attention + split merge per layer
+    return step, data
 
 
 def gqa1(da, torch, seed, dev):
@@ -135,7 +137,9 @@ def gqa1(da, torch, seed, dev):
            "num_kv_heads": hkv, "head_dim": d, "valid_len": L}
     st = Stage("attention", [one], kv + 2 * hq * d * 2,
                "decode_kernel + merge_kernel (gqa_decode_attn)")
-    return Step("gqa1", cfg, kv, kv + 2 * hq * d * 2, [st]), c
+    step = Step("gqa1", cfg, kv, kv + 2 * hq * d * 2, [st])
+    step.kernels_per_step = 2
+    return step, c
 
 
 def paged(da, torch, seed, dev):
@@ -740,6 +744,18 @@ MAKERS = {
 CAL_BYTES = 4 << 30
 
 
+def launch_floor(torch, dev, flush, n_kernels, steps):
+    """Step time of `n_kernels` one-element fill kernels launched the way the
+    step's calls are (directly, or replayed from one captured graph), with the
+    same cache flush: the launch-only floor of a step with that many dependent
+    kernels, none of which moves data."""
+    t = torch.zeros(1, dtype=torch.float32, device=dev)
+    fns = [lambda: t.fill_(1.0)] * n_kernels
+    ms, how = time_calls(torch, fns, steps, 3, flush)
+    return {"kernels": n_kernels, "kernel": "one-element fill (torch)", "launch": how,
+            "us_per_step": round(statistics.median(ms) * 1e3, 3)}
+
+
 def read_calibration(da, torch, dev, flush, reps=10):
     """HBM read rate of the library's streaming-read calibration kernel over a
     4 GiB buffer (cache flushed before each rep, median): the practical read
@@ -900,6 +916,12 @@ def main():
                 "step_us_separate_append", "us_per_step_graph"):
         if key in r:
             line[key] = r[key]
+    if hasattr(step, "kernels_per_step"):
+        # latency-bound steps: what the same number of launches costs with no
+        # data, and what the step's bytes cost at the calibrated read rate
+        fl = launch_floor(torch, dev, flush, step.kernels_per_step, max(10, args.steps // 2))
+        fl["bytes_at_calibrated_rate_us"] = round(step.algo_bytes / (cal["read_gbs"] * 1e3), 3)
+        line["launch_floor"] = fl
     if "dense_same_shape_gbs" in r:
         line["dense_same_shape_pct_calibration"] = round(
             100 * r["dense_same_shape_gbs"] / cal["read_gbs"], 2)
