@@ -616,8 +616,10 @@ def test_repeat_kv_from_paged_cache(da):
 
 def test_graph_replays_match_eager(da):
     """The calls captured in a HIP graph (dense decode with append, the fused
-    Quest step, sparse attention) give the eager results on every replay,
-    with unrelated eager work and synchronisations between the replays."""
+    Quest step with a top-K launch and sparse attention, and the Quest step
+    as launched by default: scores only, then the attention that selects its
+    own pages) give the eager results on every replay, with unrelated eager
+    work and synchronisations between the replays."""
     case = workloads.dense_case(980, 2, 32, 8, 128, 2048, [2048, 1500], with_new=True)
     s, budget = 16, 256
     q, sl = dev(case.q), dev(case.seqlens)
@@ -632,8 +634,11 @@ def test_graph_replays_match_eager(da):
 
     ws, qws = da.Workspace(), da.Workspace()
     idx = torch.empty((2, 8, budget // s), dtype=torch.int32, device=DEV)
+    idx_f = torch.empty_like(idx)
+    scores = torch.empty((2, 8, 2048 // s), dtype=torch.float32, device=DEV)
     out_d = torch.empty_like(q)
     out_s = torch.empty_like(q)
+    out_f = torch.empty_like(q)
 
     def step(k, v, meta):
         da.gqa_decode_attn(q, k, v, sl, k_new=kn, v_new=vn, out=out_d, workspace=ws)
@@ -641,11 +646,20 @@ def test_graph_replays_match_eager(da):
                                    page_idx=idx, workspace=qws)
         da.quest_sparse_decode_attn(q, k, v, sl, idx, budget_tokens=budget, page_size=s,
                                     out=out_s, workspace=ws)
+        # the append again (idempotent), scores only, then the selecting attention
+        da.quest_append_score_topk(q, k, v, meta, sl, kn, vn, page_size=s, budget_tokens=budget,
+                                   page_scores=scores, select=False, workspace=qws)
+        da.quest_select_sparse_decode_attn(q, k, v, sl, scores, budget_tokens=budget,
+                                           page_size=s, page_idx=idx_f, out=out_f, workspace=ws)
 
     k, v, meta = fresh()
     step(k, v, meta)                       # eager reference (appends are idempotent)
     torch.cuda.synchronize()
-    want = (host(out_d).copy(), host(out_s).copy(), host(idx).copy(), host(meta).copy())
+    want = (host(out_d).copy(), host(out_s).copy(), host(idx).copy(), host(meta).copy(),
+            host(out_f).copy(), host(idx_f).copy())
+    # the two Quest paths choose the same pages and give the same output
+    assert np.array_equal(want[5], want[2])
+    assert np.array_equal(want[4].view(np.uint16), want[1].view(np.uint16))
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -659,12 +673,15 @@ def test_graph_replays_match_eager(da):
     for rep in range(4):
         out_d.zero_()
         out_s.zero_()
+        out_f.zero_()
         idx.fill_(-7)
+        idx_f.fill_(-7)
+        scores.fill_(float("nan"))
         noise.mul_(1.0001).add_(1.0)        # unrelated eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = (host(out_d), host(out_s), host(idx), host(meta))
+        got = (host(out_d), host(out_s), host(idx), host(meta), host(out_f), host(idx_f))
         for a, b in zip(got, want):
             assert np.array_equal(a, b), rep
 
