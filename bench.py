@@ -422,16 +422,26 @@ def _baseline(bytes_done, elapsed, sample):
             "kind": "oracle", "sample": sample, "seconds": round(elapsed, 3)}
 
 
-def kernel_source_digest():
-    """Hash of the kernel sources: the committed counter summary is used only
-    while it was taken on these exact kernels."""
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed, so that
+    editing a comment does not change the digest."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_digest(root=None):
+    """Hash of the kernel sources' code (comments and whitespace ignored): the
+    committed counter summary is used only while it was taken on these exact
+    kernels."""
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "decode_attention_folded_amd", "csrc")
+    csrc = os.path.join(root or ROOT, "decode_attention_folded_amd", "csrc")
     for name in ("attention_impl.h", "decode_kernel.hip", "decode_select.hip", "topk.h",
                  "quest_kernels.hip", "device_common.h", "kernels.h"):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

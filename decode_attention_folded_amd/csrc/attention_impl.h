@@ -666,9 +666,9 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // Merge kernel: one workgroup per (b, kv) unit, one thread per output element
-// of the unit's G rows (G * D threads, 64 to 1024), so every thread merges a
-// batch of up to 32 splits with one round of loads.
-// Leading scalar arguments as in the attention kernel: what the first batch
+// of the unit's G rows (G * D threads, 64 to 1024); up to 48 splits are merged
+// with one round of loads (merge_partials).
+// Leading scalar arguments as in the attention kernel: what the first round
 // of partial loads needs.
 template <int D, int G, bool SPARSE>
 __global__ void __launch_bounds__(G * D)

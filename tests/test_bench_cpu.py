@@ -58,14 +58,16 @@ def test_counter_traffic_without_a_summary(tmp_path, monkeypatch):
 
 
 @pytest.mark.parametrize("name", ["attention_impl.h", "topk.h", "quest_kernels.hip"])
-def test_digest_changes_with_a_kernel_source(tmp_path, monkeypatch, name):
+def test_digest_follows_the_code_not_the_comments(tmp_path, name):
     import shutil
     src = os.path.join(ROOT, "decode_attention_folded_amd", "csrc")
     dst = tmp_path / "decode_attention_folded_amd" / "csrc"
     shutil.copytree(src, dst)
-    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    before = bench.kernel_source_digest()
-    assert before == bench.kernel_source_digest()
+    before = bench.kernel_source_digest(str(tmp_path))
+    assert before == bench.kernel_source_digest(ROOT)
     with open(dst / name, "a") as f:
-        f.write("\n// edited\n")
-    assert bench.kernel_source_digest() != before
+        f.write("\n// a comment\n/* and a\n   block comment */\n")
+    assert bench.kernel_source_digest(str(tmp_path)) == before
+    with open(dst / name, "a") as f:
+        f.write("\nstatic const int digest_probe = 1;\n")
+    assert bench.kernel_source_digest(str(tmp_path)) != before
