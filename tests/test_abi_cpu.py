@@ -235,3 +235,47 @@ def test_product_path_never_uses_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle." not in text, f
+
+
+def _planned_splits(units, max_keys, page_list, num_splits=0):
+    """The split plan as documented: 16-key tiles; without an explicit count,
+    chunks of at least 8 tiles sized for about 256 workgroups, at most 128
+    tiles when the chunk reads a page list and 256 otherwise."""
+    tiles = max(1, -(-max_keys // 16))
+    if num_splits > 0:
+        tps = -(-tiles // num_splits)
+    else:
+        tps = max(-(-(units * tiles) // 256), 8)
+    tps = min(max(tps, 1), 128 if page_list else 256, tiles)
+    return -(-tiles // tps)
+
+
+def _plan_bytes(units, splits, rows, d):
+    ml = -(-(units * splits * rows * 2 * 4) // 256) * 256
+    return ml + units * splits * rows * d * 4
+
+
+# (desc fields, Hq, budget tokens, explicit splits, page list, longest key stream, splits)
+PLAN_CASES = [
+    (dict(batch=1, num_kv_heads=8, head_dim=64, capacity=4096), 32, 0, 0, False, 4096, 32),
+    (dict(batch=8, num_kv_heads=8, head_dim=128, capacity=131072), 32, 0, 0, False, 131072, 32),
+    (dict(batch=64, num_kv_heads=8, head_dim=128, page_table=FAKE, page_size=16, max_pages=2048,
+          num_pages=70000), 32, 0, 0, True, 32768, 16),
+    (dict(batch=8, num_kv_heads=8, head_dim=128, capacity=131072), 32, 4096, 0, True, 4096, 4),
+    (dict(batch=1, num_kv_heads=32, head_dim=128, capacity=32768), 32, 2048, 0, True, 2048, 8),
+    (dict(batch=2, num_kv_heads=8, head_dim=128, capacity=4096), 32, 0, 7, False, 4096, 7),
+    (dict(batch=2, num_kv_heads=8, head_dim=64, capacity=1000, page_size=16), 32, 4096, 0, True,
+     1008, 8),
+]
+
+
+@pytest.mark.parametrize("fields,hq,budget,splits,page_list,max_keys,want_splits", PLAN_CASES)
+def test_workspace_follows_the_split_plan(lib, fields, hq, budget, splits, page_list, max_keys,
+                                          want_splits):
+    desc = _desc(**fields)
+    units = desc.batch * desc.num_kv_heads
+    got_splits = _planned_splits(units, max_keys, page_list, splits)
+    assert got_splits == want_splits  # the rule itself, on the workloads' shapes
+    out = ctypes.c_size_t()
+    assert lib.da_workspace_size(ctypes.byref(desc), hq, budget, splits, ctypes.byref(out)) == 0
+    assert out.value == _plan_bytes(units, want_splits, hq // desc.num_kv_heads, desc.head_dim)
