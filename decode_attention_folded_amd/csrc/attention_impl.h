@@ -218,7 +218,7 @@ __global__ void __launch_bounds__(kThreads)
                   int chunk_geom, AttnLaunch a) {
   constexpr bool SELECT = SEL_R > 0;
   static_assert(!SELECT || SPARSE, "page selection feeds the selected-page stream");
-  static_assert(!DRAIN || (!PAGED && !SPARSE), "the draining ring is built for the contiguous dense stream");
+  static_assert(!DRAIN || !PAGED, "the draining ring is built for contiguous caches");
   static_assert(!SELECT || kThreads == kTopkThreads, "one workgroup shape for both parts");
   constexpr int NCK = Layout<D>::NCK;
   constexpr int NCV = Layout<D>::NCV;
@@ -403,10 +403,11 @@ __global__ void __launch_bounds__(kThreads)
 
   // Masked keys, and the ring's loads past the chunk, read a row that holds
   // this sequence's data instead of their own slot, so the value multiplied
-  // by their zero weight is finite.  Contiguous dense stream: the chunk's
-  // first row (valid, since the chunk starts below L; this workgroup loads it
-  // first, so these loads hit in cache instead of waiting on a cold row at the
-  // end of the loop).  Otherwise token 0 of the sequence; a page-table entry
+  // by their zero weight is finite.  Contiguous cache: the chunk's first row
+  // (dense: row key_begin; chosen pages: the first row of the chunk's first
+  // chosen page), which is valid and which this workgroup loads first, so
+  // these loads hit in cache instead of waiting on a cold row at the end of
+  // the loop.  Paged cache: token 0 of the sequence; a page-table entry
   // outside the pool falls back to pool page 0, which always exists.
   const bool has_new = a.k_new != nullptr;
   int64_t safe_off;
@@ -422,7 +423,10 @@ __global__ void __launch_bounds__(kThreads)
     safe_off = (unit * a.cache_stride + key_begin) * D;
     safe_is_new = has_new && key_begin >= L - 1;
   } else {
-    safe_off = unit * a.cache_stride * D;
+    // the chunk's list was staged above; an entry that names no page falls
+    // back to token 0
+    const int first_page = s_page[0];
+    safe_off = (unit * a.cache_stride + (first_page >= 0 ? (first_page << shift) : 0)) * D;
     safe_is_new = has_new;
   }
 
@@ -713,23 +717,29 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
   // tiles per chunk < 2^16 (at most kMaxTilesPerSplitContiguous)
   const int chunk_geom = a.tiles_per_split | (a.page_shift << 16);
   const dim3 grid((uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads);
-  // Short contiguous dense chunks (at most two ring rounds per wave, such as
-  // a few thousand keys split over the chip) use the draining ring; long
-  // chunks keep the plain one (the drain measured 1.5% slower on them).
-  const bool drain = !PAGED && !SPARSE && a.tiles_per_split <= 2 * kStages * kWaves;
+  // Short chunks of a contiguous cache (at most two ring rounds per wave,
+  // such as a few thousand keys split over the chip) use the draining ring;
+  // long chunks keep the plain one (the drain measured 1.5% slower on them),
+  // and so does the paged cache (10% slower with it).
+  const bool drain = !PAGED && a.tiles_per_split <= 2 * kStages * kWaves;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, a.seqlens, a.q, a.k, a.v, list,
                        a.batch, a.num_kv_heads, list_width, chunk_geom, a);
   };
   if constexpr (SEL_R > 0) {  // the selecting variant is built with q.k on the MFMA only
-    go(decode_kernel<D, G, PAGED, SPARSE, true, SEL_R, false>);
-  } else if constexpr (!PAGED && !SPARSE) {
-    if (a.qk_mfma) {
-      if (drain) go(decode_kernel<D, G, false, false, true, 0, true>);
-      else go(decode_kernel<D, G, false, false, true, 0, false>);
+    if constexpr (!PAGED) {
+      if (drain) go(decode_kernel<D, G, false, SPARSE, true, SEL_R, true>);
+      else go(decode_kernel<D, G, false, SPARSE, true, SEL_R, false>);
     } else {
-      if (drain) go(decode_kernel<D, G, false, false, false, 0, true>);
-      else go(decode_kernel<D, G, false, false, false, 0, false>);
+      go(decode_kernel<D, G, PAGED, SPARSE, true, SEL_R, false>);
+    }
+  } else if constexpr (!PAGED) {
+    if (a.qk_mfma) {
+      if (drain) go(decode_kernel<D, G, false, SPARSE, true, 0, true>);
+      else go(decode_kernel<D, G, false, SPARSE, true, 0, false>);
+    } else {
+      if (drain) go(decode_kernel<D, G, false, SPARSE, false, 0, true>);
+      else go(decode_kernel<D, G, false, SPARSE, false, 0, false>);
     }
   } else if (a.qk_mfma) {
     go(decode_kernel<D, G, PAGED, SPARSE, true, 0, false>);
