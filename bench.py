@@ -248,6 +248,7 @@ def quest(da, torch, seed, dev, long_ctx):
            "head_dim": d, "seq_len": L, "page_size": s, "budget_tokens": budget,
            "k_pages": k_sel}
     st = Step("quest128k" if long_ctx else "quest32k", cfg, kv_bytes, algo, stages)
+    st.kernels_per_step = 3  # page scores, selecting attention, split merge
     st.dense_fn = dense
     # the same step with the top-K as its own launch, and (128K) with the
     # append as its own launch too, for comparison
@@ -927,8 +928,8 @@ def main():
         if key in r:
             line[key] = r[key]
     if hasattr(step, "kernels_per_step"):
-        # latency-bound steps: what the same number of launches costs with no
-        # data, and what the step's bytes cost at the calibrated read rate
+        # what the same number of dependent launches costs with no data, and
+        # what the step's bytes cost at the calibrated read rate
         fl = launch_floor(torch, dev, flush, step.kernels_per_step, max(10, args.steps // 2))
         fl["bytes_at_calibrated_rate_us"] = round(step.algo_bytes / (cal["read_gbs"] * 1e3), 3)
         line["launch_floor"] = fl
