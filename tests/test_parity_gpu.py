@@ -121,6 +121,32 @@ def test_dense_append(da):
         assert np.array_equal(kh[b, :, :lb - 1], case.k[b, :, :lb - 1])
 
 
+@pytest.mark.parametrize("with_new", [True, False])
+@pytest.mark.parametrize("num_splits", [32, 11, 10])
+def test_chunk_edges_and_the_appended_slot(da, with_new, num_splits):
+    """Chunks of 8 and 24 tiles (the draining ring for short chunks) and of 26
+    (the plain ring), with sequences whose appended slot L - 1 is exactly the
+    first key of a chunk (L = 1, 129, 257 with 128-key chunks) or inside one.
+    Masked keys and the ring's loads past a chunk read the chunk's first row,
+    except where that row is the slot being written; the slot L - 1 is
+    poisoned with NaN before the append, so reading it there would show."""
+    lens = [4096, 3000, 257, 129, 200, 1]
+    case = workloads.dense_case(990 + num_splits, len(lens), 16, 4, 64, 4096, lens,
+                                with_new=with_new)
+    if with_new:
+        for b, lb in enumerate(lens):
+            case.k[b, :, lb - 1] = np.nan
+            case.v[b, :, lb - 1] = np.nan
+    got, _, _ = run_dense(da, case, num_splits=num_splits, with_new=with_new)
+    if with_new:
+        k2, v2 = oracle.append_kv(case.k, case.v, case.seqlens, case.k_new, case.v_new)
+    else:
+        k2, v2 = case.k, case.v
+    want = oracle.decode_attention(case.q, k2, v2, case.seqlens, case.scale)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, want) <= ATOL
+
+
 def test_dense_empty_and_zero_batch(da):
     case = workloads.dense_case(10, 3, 8, 2, 64, 64, [0, 5, 0])
     got, _, _ = run_dense(da, case)
