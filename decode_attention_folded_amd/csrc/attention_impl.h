@@ -211,6 +211,10 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
 // the first split also writes the choice out.  All workgroups of a unit make
 // the same integer decisions on the same scores, so this equals a separate
 // top-K launch followed by the selected-page attention, with one launch less.
+//
+// DRAIN (contiguous cache, chunks of at most two ring rounds per wave): the
+// ring's last round issues no loads past the chunk.  The arithmetic is the
+// same as without it, so both variants give bitwise equal results.
 template <int D, int G, bool PAGED, bool SPARSE, bool QK_MFMA, int SEL_R, bool DRAIN>
 __global__ void __launch_bounds__(kThreads)
     decode_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
