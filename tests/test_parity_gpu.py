@@ -192,6 +192,44 @@ def test_paged_parity(da, page_size, d, g):
     assert max_err(got, want) <= ATOL
 
 
+@pytest.mark.parametrize("page_size", [8, 16])
+def test_paged_append(da, page_size):
+    """Fused append on a paged cache: the new row lands in slot (L - 1) mod S
+    of the sequence's page (L - 1) / S in the pool (poisoned with NaN before),
+    and attention includes it; splits forced so chunks start at page starts."""
+    hkv, g, d = 4, 4, 64
+    lens = [1500, 129, 17, 1]
+    max_pages = (1500 + page_size - 1) // page_size
+    case = workloads.paged_case(260 + page_size, len(lens), hkv * g, hkv, d, page_size,
+                                max_pages, lens, spare_pages=2)
+    rng = np.random.default_rng([260, page_size])
+    k_new = rng.standard_normal((len(lens), hkv, d), dtype=np.float32).astype(np.float16)
+    v_new = rng.standard_normal((len(lens), hkv, d), dtype=np.float32).astype(np.float16)
+    k_pool, v_pool = case.k.copy(), case.v.copy()
+    for b, lb in enumerate(lens):
+        phys = case.page_table[b, (lb - 1) // page_size]
+        k_pool[phys, :, (lb - 1) % page_size] = np.nan
+        v_pool[phys, :, (lb - 1) % page_size] = np.nan
+    k_dev, v_dev = dev(k_pool), dev(v_pool)
+    for splits in (0, 16):
+        out = da.gqa_decode_attn(dev(case.q), k_dev, v_dev, dev(case.seqlens), k_new=dev(k_new),
+                                 v_new=dev(v_new), page_table=dev(case.page_table),
+                                 page_size=page_size, num_splits=splits)
+        torch.cuda.synchronize()
+        kc = oracle.gather_paged(case.k, case.page_table, page_size, case.capacity)
+        vc = oracle.gather_paged(case.v, case.page_table, page_size, case.capacity)
+        k2, v2 = oracle.append_kv(kc, vc, case.seqlens, k_new, v_new)
+        want = oracle.decode_attention(case.q, k2, v2, case.seqlens, case.scale)
+        got = host(out).astype(np.float64)
+        assert np.all(np.isfinite(got)), splits
+        assert max_err(got, want) <= ATOL, splits
+    kh, vh = host(k_dev), host(v_dev)
+    for b, lb in enumerate(lens):
+        phys = case.page_table[b, (lb - 1) // page_size]
+        assert np.array_equal(kh[phys, :, (lb - 1) % page_size], k_new[b])
+        assert np.array_equal(vh[phys, :, (lb - 1) % page_size], v_new[b])
+
+
 # ------------------------------------------------------------ quest metadata
 
 
