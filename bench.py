@@ -3,21 +3,31 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
-Prints ONE JSON line.  A "step" is one pass of the whole hot path over one
-batch of synthetic inputs already resident in HBM:
+Prints ONE JSON line.  A "step" is one pass of the hot path over one batch of
+synthetic inputs already resident in HBM.
 
-* exaone30 (default): 30 sequential decode-attention layers shaped like
-  EXAONE 4.0 1.2B (Hq 32, Hkv 8, D 64, fp16 cache [8, 4096, 64] per layer,
-  3000 valid keys, the step's K/V row appended at slot 2999 inside the
-  attention kernel), captured once in a HIP graph and replayed per step.
+* long_context (default): the long-context Quest GQA workload, B 8, Hq 32,
+  Hkv 8, D 128, L 131072 (contiguous fp16 cache [8, 8, 131072, 128], 16
+  planted pages per KV head).  The headline step is folded decode attention
+  over the whole context with the step's K/V row appended at slot 131071
+  (gqa_decode_attn: decode kernel + split merge); `value` is its KV GB/s and
+  `roofline` its achieved rate.  Beside it: the Quest step at the same shape
+  (K/V row and page-metadata append fused into the page scores, then top-K +
+  attention over the 256 chosen pages + split merge), its stages, each
+  kernel's fraction of peak, and its time over the dense step next to the
+  byte model 1/S + B/L = 3/32.  Secondary legs (shorter runs): the EXAONE-
+  shaped 30-layer step, the batched paged decode, the 32K Llama2-7B-shaped
+  Quest step and one GQA layer.
+* exaone30:    30 sequential decode-attention layers shaped like EXAONE 4.0
+  1.2B (Hq 32, Hkv 8, D 64, fp16 cache [8, 4096, 64] per layer, 3000 valid
+  keys, the step's K/V row appended at slot 2999 inside the attention
+  kernel), captured once in a HIP graph and replayed per step.
 * gqa1:        one layer, B 1, Hq 32, Hkv 8, D 64, 4096 keys.
 * paged:       B 64, Hq 32, Hkv 8, D 128, page size 16, lengths U[1024, 32768].
 * quest32k:    Llama2-7B-shaped, B 1, H 32, D 128, L 32768, budget 2048:
                page score + top-K + sparse attention (dense at the same
                shape is reported beside it).
-* quest128k:   B 8, Hq 32, Hkv 8, D 128, L 131072, budget 4096: KV append +
-               metadata append, page score + top-K, sparse attention (and
-               dense at the same shape).
+* quest128k:   the Quest step of the long-context workload as the line.
 
 Before every timed step a 1 GiB buffer is written (outside the step's events)
 so that neither L2 nor the 256 MiB Infinity Cache holds the inputs.  A step
@@ -25,15 +35,11 @@ of at most three calls is launched directly on the stream (the host enqueues
 it while the flush kernel runs); a longer step is captured once in a HIP graph
 and replayed.  Step time is the median over the K steps of HIP events around
 the step on the launching stream.  `value` is the KV bytes the step must read
-divided by the step time.  A step is made of stages (the dense workloads: one
-stage of attention calls; Quest: page score + top-K with the fused append,
-sparse attention).  The roofline entry is the dominant stage: its algorithmic
-bytes divided by its time, which for a one-stage step is the step time itself
-and otherwise the median time of the stage's calls alone after a flush.  One
-attention call runs the attention kernel and the small split-merge kernel
-(or the score and top-K kernels), so both count.  The CPU baseline is the
-fp64 NumPy oracle (1 BLAS thread) on a bounded sample of the same workload,
-timed on the host.
+divided by the step time.  One attention call runs the attention kernel and
+the small split-merge kernel (or the score and top-K kernels), so both count.
+The CPU baseline is the fp64 NumPy oracle on a bounded sample of the same
+workload, timed on the host's cores (one worker thread per sampled unit, up
+to the cores available, one BLAS thread each; median of 3 passes).
 """
 
 import argparse
@@ -58,13 +64,13 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="exaone30",
-                    choices=["exaone30", "gqa1", "paged", "quest32k", "quest128k",
-                             "repeat_kv_ab", "quest_sweep", "multi_query"])
+    ap.add_argument("--workload", default="long_context",
+                    choices=["long_context", "exaone30", "gqa1", "paged", "quest32k",
+                             "quest128k", "repeat_kv_ab", "quest_sweep", "multi_query"])
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-long-context", action="store_true",
-                    help="skip the 128K Quest/dense leg of the default workload")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the secondary workloads of the default line")
     ap.add_argument("--seed", type=int, default=2)
     return ap.parse_args()
 
@@ -176,7 +182,11 @@ def quest(da, torch, seed, dev, long_ctx):
                                plant_page_size=s, with_new=long_ctx)
     P = L // s
     meta = torch.zeros((b, hkv, P, 2, d), dtype=torch.float16, device=dev)
-    da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], n_new=L, page_size=s)
+    # the metadata state before the step: with an append, the step's token is
+    # key L - 1, so the state covers keys [0, L - 1) (the slot the append
+    # overwrites is not a key yet)
+    built = c["seqlens"] - 1 if long_ctx else c["seqlens"]
+    da.quest_meta_append(c["k"], c["v"], meta, built, n_new=L, page_size=s)
     k_sel = budget // s
     idx = torch.empty((b, hkv, k_sel), dtype=torch.int32, device=dev)
     scores = torch.empty((b, hkv, P), dtype=torch.float32, device=dev)
@@ -221,6 +231,10 @@ def quest(da, torch, seed, dev, long_ctx):
     def dense():
         da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], out=dense_out, workspace=dws)
 
+    def dense_append():   # dense decode attention with the step's K/V row appended
+        da.gqa_decode_attn(c["q"], c["k"], c["v"], c["seqlens"], k_new=c["k_new"],
+                           v_new=c["v_new"], out=dense_out, workspace=dws)
+
     units = b * hkv
     meta_bytes = units * P * 2 * d * 2
     sel_bytes = units * k_sel * s * 2 * d * 2
@@ -249,13 +263,18 @@ def quest(da, torch, seed, dev, long_ctx):
            "k_pages": k_sel}
     st = Step("quest128k" if long_ctx else "quest32k", cfg, kv_bytes, algo, stages)
     st.kernels_per_step = 3  # page scores, selecting attention, split merge
-    st.dense_fn = dense
+    st.dense_fn = dense_append if long_ctx else dense
+    c["quest_out"], c["dense_out"], c["idx"], c["scores"], c["meta"] = (out, dense_out, idx,
+                                                                        scores, meta)
     # the same step with the top-K as its own launch, and (128K) with the
     # append as its own launch too, for comparison
     st.variants = {"separate_topk": [append_select if long_ctx else select, attend]}
     if long_ctx:
         st.variants["separate_append"] = [append, select, attend]
     st.dense_bytes = dense_bytes
+    # the dense step's algorithmic bytes: K/V of every valid key, the appended
+    # row (read from k_new/v_new and written), Q and the output
+    st.dense_algo_bytes = dense_bytes + (units * 2 * 2 * d * 2 if long_ctx else 0) + qo_bytes
     st.byte_model = {"meta_bytes": meta_bytes, "selected_bytes": sel_bytes,
                      "dense_bytes": dense_bytes,
                      "ratio_model": 1.0 / s + budget / L}
@@ -333,7 +352,9 @@ def time_stages(torch, graphs, steps, warmup, flush):
 
 
 def cpu_baseline(step, data, seed):
-    """The fp64 oracle on a bounded sample of the same workload, 1 BLAS thread."""
+    """The fp64 oracle on a bounded sample of a secondary workload, in one
+    thread with one BLAS thread (the default line's baseline is
+    long_context_cpu_baseline)."""
     from threadpoolctl import threadpool_limits
     with threadpool_limits(1):
         return _cpu_baseline(step, data)
@@ -419,8 +440,10 @@ def torch_index(pages):
 
 
 def _baseline(bytes_done, elapsed, sample):
+    # these workloads' oracle legs run in one thread with one BLAS thread
     return {"value": round(bytes_done / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "sample": sample, "seconds": round(elapsed, 3)}
+            "kind": "oracle", "sample": sample, "seconds": round(elapsed, 3),
+            "host_cores": len(os.sched_getaffinity(0)), "blas_threads": 1}
 
 
 def _code_only(text):
@@ -745,6 +768,283 @@ def quest_sweep(da, torch, seed, dev, steps, warmup, flush):
             "sweep": sweep, "stack_32_layers": stack}
 
 
+def sample_units(batch, hkv, n):
+    """(b, kv) units spread over the batch and the KV heads."""
+    units = []
+    for i in range(n):
+        b = i % batch
+        units.append((b, (3 * i + 1 + i // batch) % hkv))
+    return units
+
+
+def host_threads():
+    """Cores this process may run on, and the BLAS threads NumPy would use."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"), default=1)
+    except ImportError:
+        blas = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    return cores, blas
+
+
+def long_context_cpu_baseline(step, c, units, reps=3):
+    """The fp64 oracle on sampled (b, kv) units of the long-context workload,
+    and the GPU's results on those units checked against it.
+
+    One oracle step per unit: the K/V row append and repeat_kv attention over
+    the whole context (the dense step); and the Quest step: metadata update
+    for the new key, page scores, top-K, attention over the chosen pages.  The
+    units run in parallel worker threads (NumPy releases the GIL in its array
+    loops), one per unit up to the host's cores, each with one BLAS thread.
+    Each of the dense and Quest passes is timed three times; the median
+    counts.  The GPU outputs are those of the last timed step (the inputs do
+    not change between steps and the append is idempotent)."""
+    import concurrent.futures
+    import numpy as np
+    import oracle
+    from oracle import quest as oquest
+    from threadpoolctl import threadpool_limits
+
+    cfg = step.config
+    L, S, D = cfg["seq_len"], cfg["page_size"], cfg["head_dim"]
+    G = cfg["num_q_heads"] // cfg["num_kv_heads"]
+    K = cfg["budget_tokens"] // S
+    P = L // S
+    scale = 1.0 / math.sqrt(D)
+    host = []
+    for (b, kv) in units:   # host copies of the unit (outside the timed passes)
+        u = {"q": c["q"][b:b + 1, kv * G:(kv + 1) * G].cpu().numpy(),
+             "k": c["k"][b:b + 1, kv:kv + 1].cpu().numpy(),
+             "v": c["v"][b:b + 1, kv:kv + 1].cpu().numpy(),
+             "k_new": c["k_new"][b:b + 1, kv:kv + 1].cpu().numpy(),
+             "v_new": c["v_new"][b:b + 1, kv:kv + 1].cpu().numpy(),
+             "lens": np.array([L], np.int32),
+             "gpu_dense": c["dense_out"][b, kv * G:(kv + 1) * G].float().cpu().numpy(),
+             "gpu_quest": c["quest_out"][b, kv * G:(kv + 1) * G].float().cpu().numpy(),
+             "gpu_idx": c["idx"][b:b + 1, kv:kv + 1].cpu().numpy()}
+        # the resident metadata state the step updates (built once, untimed)
+        u["meta"] = oquest.build_metadata(u["k"], u["lens"], S, P)
+        host.append(u)
+
+    def dense_unit(u):
+        k2, v2 = oracle.append_kv(u["k"], u["v"], u["lens"], u["k_new"], u["v_new"])
+        return oracle.decode_attention(u["q"], k2, v2, u["lens"], scale)[0]
+
+    def quest_unit(u):
+        k2, v2 = oracle.append_kv(u["k"], u["v"], u["lens"], u["k_new"], u["v_new"])
+        meta = oquest.append_metadata(u["meta"], k2, u["lens"], 1, S)
+        scores = oquest.page_scores(u["q"], meta, u["lens"], S)
+        idx = oquest.select_pages(scores, u["lens"], S, K)
+        out = oquest.sparse_decode_attention(u["q"], k2, v2, u["lens"], idx, S, scale)[0]
+        return scores, idx, out, k2, v2
+
+    cores, _ = host_threads()
+    workers = max(1, min(cores, len(host)))
+
+    def timed_pass(fn):
+        times, res = [], None
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                res = list(ex.map(fn, host))
+                times.append(time.perf_counter() - t0)
+        return statistics.median(times), res
+
+    with threadpool_limits(1):
+        t_dense, dense_res = timed_pass(dense_unit)
+        t_quest, quest_res = timed_pass(quest_unit)
+        # attention over the GPU's own choice (untimed; the parity check)
+        quest_err = 0.0
+        idx_exact = swaps = violations = 0
+        for u, (scores, idx, out, k2, v2) in zip(host, quest_res):
+            g = [int(p) for p in u["gpu_idx"][0, 0] if p >= 0]
+            w = [int(p) for p in idx[0, 0] if p >= 0]
+            if g == w:
+                idx_exact += 1
+                want = out
+            else:
+                kth = np.sort(scores[0, 0])[::-1][K - 1]
+                diff = set(g) ^ set(w)
+                swaps += len(diff) // 2
+                violations += sum(1 for p in diff
+                                  if abs(scores[0, 0, p] - kth) > 1e-5 * abs(kth))
+                # the oracle's attention over the pages the GPU chose
+                want = oquest.sparse_decode_attention(u["q"], k2, v2, u["lens"], u["gpu_idx"],
+                                                      S, scale)[0]
+            quest_err = max(quest_err, float(np.max(np.abs(u["gpu_quest"] - want))))
+    dense_err = max(float(np.max(np.abs(u["gpu_dense"] - r))) for u, r in zip(host, dense_res))
+    unit_kv = L * 2 * D * 2
+    quest_unit_bytes = step.kv_bytes // (cfg["batch"] * cfg["num_kv_heads"])
+    cores, blas = host_threads()
+    return {
+        "value": round(len(host) * unit_kv / t_dense / 1e9, 6), "unit": "GB/s",
+        "cores": workers, "kind": "oracle",
+        "sample": (f"{len(host)} of the {cfg['batch'] * cfg['num_kv_heads']} (b, kv) units, "
+                   f"one oracle step each (append + repeat_kv attention over {L} keys, fp64); "
+                   "median of 3 passes"),
+        "seconds": round(t_dense, 3),
+        "host_cores": cores, "blas_threads": 1, "worker_threads": workers,
+        "quest": {"gbs": round(len(host) * quest_unit_bytes / t_quest / 1e9, 6),
+                  "seconds": round(t_quest, 3),
+                  "sample": "the same units: append, new-key metadata update, page scores, "
+                            "top-K, attention over the chosen pages (fp64); median of 3"},
+        "parity": {"units": [list(u) for u in units],
+                   "dense_max_abs_err": dense_err,
+                   "quest_max_abs_err": quest_err,
+                   "idx_exact": idx_exact, "idx_units": len(host),
+                   "idx_near_tie_swaps": swaps, "idx_rule_violations": violations,
+                   "tolerance": 2e-3},
+    }
+
+
+def summarize_leg(name, step, r):
+    """The short record of a secondary workload in the default line."""
+    out = {"workload": step.config["workload"], "us_per_step": r["us_per_step"],
+           "kv_gbs": round(r["gbs"], 1), "pct_hbm_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2),
+           "launch": r["launch"], "stage_us": r["stage_us"],
+           "algorithmic_bytes_per_step": step.algo_bytes}
+    for key in ("quest_over_dense_time", "dense_same_shape_us", "dense_same_shape_pct_peak"):
+        if key in r:
+            out[key] = r[key]
+    if "byte_model" in r:
+        out["byte_model_ratio"] = r["byte_model"]["ratio_model"]
+    return out
+
+
+def long_context_line(args, torch, da, dev, flush):
+    """The default line: dense decode attention on the long-context workload
+    (value, roofline), the Quest step beside it, secondary legs, CPU
+    baseline."""
+    step, c = MAKERS["quest128k"](da, torch, args.seed, dev)
+    units = step.config["batch"] * step.config["num_kv_heads"]
+    # warm-up calls allocate every workspace before the timed loops
+    step.dense_fn()
+    for st in step.stages:
+        for f in st.fns:
+            f()
+    torch.cuda.synchronize()
+
+    # the headline step: one gqa_decode_attn call (decode kernel + merge)
+    t0 = time.perf_counter()
+    dense_ms = time_direct(torch, [step.dense_fn], args.steps, args.warmup, flush)
+    dense_wall = time.perf_counter() - t0
+    ms = statistics.median(dense_ms)
+    # the Quest step at the same shape
+    qr = measure(torch, da, dev, step, args.steps, args.warmup, flush)
+    stage_bytes = {st.name: st.bytes for st in step.stages}
+    quest_stages = {}
+    for name, us in qr["stage_us"].items():
+        gbs = stage_bytes[name] / (us * 1e-6) / 1e9
+        quest_stages[name] = {"us": us, "bytes": stage_bytes[name], "gbs": round(gbs, 1),
+                              "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    quest_ms = qr["ms"]
+    model = step.byte_model["ratio_model"]
+
+    # reference copy of known size (scales the FETCH/WRITE counters in the
+    # counter runs); not part of the timed region
+    src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+    cal = read_calibration(da, torch, dev, flush)
+    achieved = step.dense_algo_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "decode-attn KV GB/s (% HBM peak) + us/step; Quest score+topK+attn us/step",
+        "value": round(step.dense_bytes / (ms * 1e-3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in, f32 accumulate",
+        "data": "synthetic N(0,1) fp16, seeded; 16 planted pages per KV head",
+        "config": {"workload": "long_context_gqa_b8_hq32_hkv8_d128_L131072_append",
+                   "batch": 8, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                   "seq_len": step.config["seq_len"], "capacity": step.config["seq_len"],
+                   "append_slot": step.config["seq_len"] - 1,
+                   "step": "gqa_decode_attn over every valid key with the step's K/V row "
+                           "appended (decode kernel + split merge)"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 3),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": counter_traffic("long_context", "dense_attention"),
+            "frac_of_calibration": round(achieved / cal["read_gbs"], 4),
+            "kernel": "decode_kernel<128,4> + merge_kernel (gqa_decode_attn)",
+            "stage": "dense_attention",
+            "calls_per_step": 1,
+            "us_per_call": round(ms * 1e3, 3),
+            "bytes_per_call": step.dense_algo_bytes,
+            "time_source": "HIP events around the call on its stream in the timed region "
+                           "(median over steps); the call is the decode kernel and the "
+                           "split merge",
+        },
+        "us_per_step": round(ms * 1e3, 3),
+        "us_p10": round(sorted(dense_ms)[len(dense_ms) // 10] * 1e3, 3),
+        "us_p90": round(sorted(dense_ms)[(len(dense_ms) * 9) // 10] * 1e3, 3),
+        "kv_bytes_per_step": step.dense_bytes,
+        "algorithmic_bytes_per_step": step.dense_algo_bytes,
+        "pct_hbm_peak": round(100 * step.dense_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "cache_flush_between_steps": flush is not None,
+        "launch": "the step's call launched directly on the stream",
+        "timed_wall_s": round(dense_wall, 3),
+        "quest": {
+            "workload": step.config["workload"],
+            "us_per_step": qr["us_per_step"],
+            "us_p10": qr["us_p10"],
+            "us_p90": qr["us_p90"],
+            "kv_bytes_per_step": step.kv_bytes,
+            "algorithmic_bytes_per_step": step.algo_bytes,
+            "gbs": round(step.algo_bytes / (quest_ms * 1e-3) / 1e9, 1),
+            "frac": round(step.algo_bytes / (quest_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stages": quest_stages,
+            "stage_time_source": "HIP events around each stage's call alone after a cache "
+                                 "flush (median); each carries its own first-launch latency",
+            "us_per_step_separate_topk": qr["step_us_separate_topk"],
+            "us_per_step_separate_append": qr["step_us_separate_append"],
+            "quest_over_dense_time": round(quest_ms / ms, 4),
+            "byte_model_ratio": model,
+            "over_byte_model": round(quest_ms / ms / model, 3),
+            "target_us_at_70pct": round(step.kv_bytes / (0.7 * HBM_PEAK_GBS * 1e3), 3),
+            "units": units,
+        },
+        "calibration": cal,
+        "dense_pct_calibration": round(100 * step.dense_bytes / (ms * 1e-3) / 1e9
+                                       / cal["read_gbs"], 2),
+    }
+    fl = launch_floor(torch, dev, flush, step.kernels_per_step, max(10, args.steps // 2))
+    fl["bytes_at_calibrated_rate_us"] = round(step.algo_bytes / (cal["read_gbs"] * 1e3), 3)
+    line["quest"]["launch_floor"] = fl
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = long_context_cpu_baseline(
+            step, c, sample_units(step.config["batch"], step.config["num_kv_heads"], 16))
+    del c
+    torch.cuda.empty_cache()
+
+    if not args.no_legs:
+        legs = {}
+        for name in ("exaone30", "paged", "quest32k", "gqa1"):
+            lstep, ldata = MAKERS[name](da, torch, args.seed, dev)
+            r = measure(torch, da, dev, lstep, max(10, args.steps // 2), 3, flush)
+            legs[name] = summarize_leg(name, lstep, r)
+            if hasattr(lstep, "kernels_per_step"):
+                lf = launch_floor(torch, dev, flush, lstep.kernels_per_step, 10)
+                legs[name]["launch_floor_us"] = lf["us_per_step"]
+            del ldata
+            torch.cuda.empty_cache()
+        line["legs"] = legs
+    return line
+
+
 MAKERS = {
     "exaone30": exaone30, "gqa1": gqa1, "paged": paged,
     "quest32k": lambda *a: quest(*a, long_ctx=False),
@@ -864,6 +1164,9 @@ def main():
         }
         print(json.dumps(line), flush=True)
         return 0
+    if args.workload == "long_context":
+        print(json.dumps(long_context_line(args, torch, da, dev, flush)), flush=True)
+        return 0
     step, data = MAKERS[args.workload](da, torch, args.seed, dev)
     r = measure(torch, da, dev, step, args.steps, args.warmup, flush)
 
@@ -939,32 +1242,6 @@ def main():
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step, data, args.seed)
-
-    if args.workload == "exaone30" and not args.no_long_context:
-        # The long-context Quest step (KV + metadata append, page score + top-K,
-        # sparse attention) and dense attention at the same shape, in the same
-        # run: the 32K+ side of the metric.
-        del data
-        torch.cuda.empty_cache()
-        qstep, qdata = MAKERS["quest128k"](da, torch, args.seed, dev)
-        q = measure(torch, da, dev, qstep, max(10, args.steps // 2), 3, flush)
-        line["long_context"] = {
-            "workload": qstep.config["workload"],
-            "quest_us_per_step": q["us_per_step"],
-            "quest_us_per_step_separate_topk": q["step_us_separate_topk"],
-            "quest_us_per_step_separate_append": q["step_us_separate_append"],
-            "quest_kv_gbs": round(q["gbs"], 1),
-            "stage_us": q["stage_us"],
-            "dense_same_shape_us": q["dense_same_shape_us"],
-            "dense_same_shape_gbs": q["dense_same_shape_gbs"],
-            "dense_same_shape_pct_peak": q["dense_same_shape_pct_peak"],
-            "dense_same_shape_pct_calibration": round(
-                100 * q["dense_same_shape_gbs"] / cal["read_gbs"], 2),
-            "quest_over_dense_time": q["quest_over_dense_time"],
-            "byte_model_ratio": q["byte_model"]["ratio_model"],
-        }
-        del qdata
-        torch.cuda.empty_cache()
 
     print(json.dumps(line), flush=True)
     return 0

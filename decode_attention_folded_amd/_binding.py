@@ -181,27 +181,39 @@ def _out_like(q, out):
 class Workspace:
     """A device scratch buffer that grows on demand.  It holds only per-call
     partial results, so one workspace serves any number of calls issued in
-    order on one stream."""
+    order on one stream.  Calls that may run concurrently (on different
+    streams) need different workspaces; the default workspaces below are kept
+    per stream for that reason."""
 
     def __init__(self, device=None):
         self.device = device
         self.buf = None
 
-    def get(self, nbytes, device):
+    def get(self, nbytes, device, stream=None):
+        """A buffer of at least `nbytes`.  A new buffer is allocated on
+        `stream` (default: the current stream), so the caching allocator
+        recycles a replaced buffer only in that stream's order."""
         nbytes = max(int(nbytes), 256)
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            self.buf = None
+            if stream is None:
+                self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            else:
+                with torch.cuda.stream(stream):
+                    self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         return self.buf
 
 
 _DEFAULT_WS = {}
 
 
-def _workspace(ws, device, kind="attn"):
-    # The attention calls share one default workspace; page scores get their
-    # own, so a score buffer is never overwritten by a later attention call.
+def _workspace(ws, device, kind="attn", stream=None):
+    # The attention calls share one default workspace per device and stream;
+    # page scores get their own, so a score buffer is never overwritten by a
+    # later attention call.  A caller-supplied workspace is used as given.
     if ws is None:
-        key = (kind, device.type, device.index)
+        s = stream if stream is not None else torch.cuda.current_stream(device)
+        key = (kind, device.type, device.index, s.cuda_stream)
         ws = _DEFAULT_WS.setdefault(key, Workspace(device))
     return ws
 
@@ -248,7 +260,7 @@ def gqa_decode_attn(q, k_cache, v_cache, seqlens, *, scale=None, k_new=None, v_n
     nbytes = ctypes.c_size_t()
     _check(lib.da_workspace_size(ctypes.byref(desc), hq, 0, num_splits, ctypes.byref(nbytes)),
            "da_workspace_size")
-    ws = _workspace(workspace, q.device).get(nbytes.value, q.device)
+    ws = _workspace(workspace, q.device, stream=stream).get(nbytes.value, q.device, stream)
     _check(lib.gqa_decode_attn(_ptr(q), ctypes.byref(desc), _ptr(seqlens), hq, scale,
                                _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(ws), ws.numel(),
                                num_splits, _stream_handle(q.device, stream)),
@@ -282,7 +294,7 @@ def gqa_decode_attn_multi(q, k_cache, v_cache, seqlens, *, scale=None, page_tabl
     nbytes = ctypes.c_size_t()
     _check(lib.da_workspace_size(ctypes.byref(desc), hq * q_len, 0, num_splits,
                                  ctypes.byref(nbytes)), "da_workspace_size")
-    ws = _workspace(workspace, q.device).get(nbytes.value, q.device)
+    ws = _workspace(workspace, q.device, stream=stream).get(nbytes.value, q.device, stream)
     _check(lib.gqa_decode_attn_multi(_ptr(q), ctypes.byref(desc), _ptr(seqlens), hq, q_len,
                                      scale, _ptr(out), _ptr(ws), ws.numel(), num_splits,
                                      _stream_handle(q.device, stream)),
@@ -390,8 +402,8 @@ def quest_page_score_topk(q, meta, seqlens, *, page_size, budget_tokens, page_id
                              page_size, q.device)
     ws = None
     if page_scores is None:
-        ws = _workspace(workspace, q.device, "scores").get(
-            quest_workspace_bytes(batch, hkv, max_pages), q.device)
+        ws = _workspace(workspace, q.device, "scores", stream).get(
+            quest_workspace_bytes(batch, hkv, max_pages), q.device, stream)
     else:
         _need(page_scores, "page_scores", torch.float32, 3)
         if tuple(page_scores.shape) != (batch, hkv, max_pages):
@@ -431,8 +443,8 @@ def quest_append_score_topk(q, k_cache, v_cache, meta, seqlens, k_new, v_new, *,
                              page_size, q.device)
     ws = None
     if page_scores is None:
-        ws = _workspace(workspace, q.device, "scores").get(
-            quest_workspace_bytes(batch, hkv, max_pages), q.device)
+        ws = _workspace(workspace, q.device, "scores", stream).get(
+            quest_workspace_bytes(batch, hkv, max_pages), q.device, stream)
     else:
         _need(page_scores, "page_scores", torch.float32, 3)
         if tuple(page_scores.shape) != (batch, hkv, max_pages):
@@ -465,7 +477,7 @@ def quest_sparse_decode_attn(q, k_cache, v_cache, seqlens, page_idx, *, budget_t
     nbytes = ctypes.c_size_t()
     _check(lib.da_workspace_size(ctypes.byref(desc), hq, budget_tokens, num_splits,
                                  ctypes.byref(nbytes)), "da_workspace_size")
-    ws = _workspace(workspace, q.device).get(nbytes.value, q.device)
+    ws = _workspace(workspace, q.device, stream=stream).get(nbytes.value, q.device, stream)
     _check(lib.quest_sparse_decode_attn(_ptr(q), ctypes.byref(desc), _ptr(seqlens),
                                         _ptr(page_idx), budget_tokens, hq, scale, _ptr(out),
                                         _ptr(ws), ws.numel(), num_splits,
@@ -500,7 +512,7 @@ def quest_select_sparse_decode_attn(q, k_cache, v_cache, seqlens, page_scores, *
     nbytes = ctypes.c_size_t()
     _check(lib.da_workspace_size(ctypes.byref(desc), hq, budget_tokens, num_splits,
                                  ctypes.byref(nbytes)), "da_workspace_size")
-    ws = _workspace(workspace, q.device).get(nbytes.value, q.device)
+    ws = _workspace(workspace, q.device, stream=stream).get(nbytes.value, q.device, stream)
     _check(lib.quest_select_sparse_decode_attn(_ptr(q), ctypes.byref(desc), _ptr(seqlens),
                                                _ptr(page_scores), page_scores.shape[2],
                                                budget_tokens, hq, scale, _ptr(page_idx),

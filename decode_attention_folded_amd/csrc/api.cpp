@@ -8,8 +8,6 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include "../../include/decode_attn.h"
 #include "kernels.h"
@@ -124,16 +122,6 @@ int max_stream_keys(const Shape& s, int budget_tokens) {
   return (int)(budget_tokens < all_pages ? budget_tokens : all_pages);
 }
 
-// q.k on the matrix cores (MFMA) unless DECODE_ATTN_QK=valu selects the
-// v_dot2 path; read once.
-bool qk_on_matrix_cores() {
-  static const bool mfma = [] {
-    const char* v = getenv("DECODE_ATTN_QK");
-    return !(v != nullptr && strcmp(v, "valu") == 0);
-  }();
-  return mfma;
-}
-
 int check_budget(const Shape& s, int budget_tokens) {
   if (!is_pow2_in(s.page_size, 8, 64)) return DA_ERR_UNSUPPORTED;
   if (budget_tokens <= 0 || budget_tokens % s.page_size != 0) return DA_ERR_BUDGET;
@@ -212,7 +200,6 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
   a.tiles_per_split = plan.tiles_per_split;
   a.max_splits = plan.max_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.qk_mfma = qk_on_matrix_cores() ? 1 : 0;
   return da::launch_decode(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
 }
 

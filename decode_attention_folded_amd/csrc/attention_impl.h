@@ -40,11 +40,9 @@
 //   V: lane holds keys (lane % 8) and (lane % 8) + 8, chunks 8*h + lane/8,
 //      h < D/64: each load instruction covers 128 contiguous bytes of each
 //      of 8 keys, and a lane accumulates only D/8 channels per query row.
-// Scores: with QK_MFMA the G query rows are replicated over the 16 rows of
-// the MFMA A operand, so every lane receives all G scores of its K key; the
-// VALU variant (v_dot2_f32_f16 over the lane's channels, then a sum over the
-// 4 lanes of the key) gives the same placement.  One DPP exchange (lane ^ 8)
-// hands each lane the scores of its two V keys.
+// Scores: the G query rows are replicated over the 16 rows of the MFMA A
+// operand, so every lane receives all G scores of its K key.  One DPP
+// exchange (lane ^ 8) hands each lane the scores of its two V keys.
 // Each lane keeps its own online-softmax state (m, l, fp32 accumulators) over
 // the keys that pass through its slots; the 8 slot states of a channel group
 // are merged at the end of the chunk, then the 4 waves through LDS.
@@ -215,7 +213,7 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
 // DRAIN (contiguous cache, chunks of at most two ring rounds per wave): the
 // ring's last round issues no loads past the chunk.  The arithmetic is the
 // same as without it, so both variants give bitwise equal results.
-template <int D, int G, bool PAGED, bool SPARSE, bool QK_MFMA, int SEL_R, bool DRAIN>
+template <int D, int G, bool PAGED, bool SPARSE, int SEL_R, bool DRAIN>
 __global__ void __launch_bounds__(kThreads)
     decode_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
                   void* v, const void* __restrict__ list, int batch, int hkv, int list_width,
@@ -265,23 +263,13 @@ __global__ void __launch_bounds__(kThreads)
   const f16* qb = reinterpret_cast<const f16*>(q) + unit * G * D;
   // MFMA A operand: row i of chain c is query g = (4c + i % 4) mod G; the lane
   // holds row lane % 16 over the k-slots of chunk 4j + ck.
-  f16x8 qa[QK_MFMA ? GC : 1][QK_MFMA ? NCK : 1];
-  // VALU operand: all G rows over the lane's K channels.
-  f16x8 qv[QK_MFMA ? 1 : G][QK_MFMA ? 1 : NCK];
-  if constexpr (QK_MFMA) {
+  f16x8 qa[GC][NCK];
 #pragma unroll
-    for (int cch = 0; cch < GC; ++cch) {
-      const int g = (4 * cch + (rk & 3)) % G;
+  for (int cch = 0; cch < GC; ++cch) {
+    const int g = (4 * cch + (rk & 3)) % G;
 #pragma unroll
-      for (int j = 0; j < NCK; ++j)
-        qa[cch][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < NCK; ++j)
-        qv[g][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
+    for (int j = 0; j < NCK; ++j)
+      qa[cch][j] = *reinterpret_cast<const f16x8*>(qb + g * D + 8 * (4 * j + ck));
   }
   // Entry i of the chunk's page list: the chosen logical page (selected-page
   // stream) and/or the physical page (paged cache), read with clamped indices.
@@ -544,33 +532,21 @@ __global__ void __launch_bounds__(kThreads)
   auto compute_stage = [&](const Stage<D>& st) {
     // scores of this lane's K key, all G rows
     float sk[G];
-    if constexpr (QK_MFMA) {
 #pragma unroll
-      for (int cch = 0; cch < GC; ++cch) {
-        f32x4 d4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int cch = 0; cch < GC; ++cch) {
+      f32x4 d4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int j = 0; j < NCK; ++j) {
-          const f16x4 blo = {st.k[j][0], st.k[j][1], st.k[j][2], st.k[j][3]};
-          const f16x4 bhi = {st.k[j][4], st.k[j][5], st.k[j][6], st.k[j][7]};
-          const f16x4 alo = {qa[cch][j][0], qa[cch][j][1], qa[cch][j][2], qa[cch][j][3]};
-          const f16x4 ahi = {qa[cch][j][4], qa[cch][j][5], qa[cch][j][6], qa[cch][j][7]};
-          d4 = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, d4, 0, 0, 0);
-          d4 = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, d4, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * cch + r < G) sk[4 * cch + r] = d4[r];
+      for (int j = 0; j < NCK; ++j) {
+        const f16x4 blo = {st.k[j][0], st.k[j][1], st.k[j][2], st.k[j][3]};
+        const f16x4 bhi = {st.k[j][4], st.k[j][5], st.k[j][6], st.k[j][7]};
+        const f16x4 alo = {qa[cch][j][0], qa[cch][j][1], qa[cch][j][2], qa[cch][j][3]};
+        const f16x4 ahi = {qa[cch][j][4], qa[cch][j][5], qa[cch][j][6], qa[cch][j][7]};
+        d4 = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, blo, d4, 0, 0, 0);
+        d4 = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bhi, d4, 0, 0, 0);
       }
-    } else {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float x = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NCK; ++j) x = dot8(qv[g][j], st.k[j], x);
-        x += lane_xor<16>(x);
-        x += lane_xor<32>(x);
-        sk[g] = x;
-      }
+      for (int r = 0; r < 4; ++r)
+        if (4 * cch + r < G) sk[4 * cch + r] = d4[r];
     }
     // scores of the two V keys of this lane: keys (lane % 8) and + 8
     float sa[G], sb[G];
@@ -730,25 +706,12 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, a.seqlens, a.q, a.k, a.v, list,
                        a.batch, a.num_kv_heads, list_width, chunk_geom, a);
   };
-  if constexpr (SEL_R > 0) {  // the selecting variant is built with q.k on the MFMA only
-    if constexpr (!PAGED) {
-      if (drain) go(decode_kernel<D, G, false, SPARSE, true, SEL_R, true>);
-      else go(decode_kernel<D, G, false, SPARSE, true, SEL_R, false>);
-    } else {
-      go(decode_kernel<D, G, PAGED, SPARSE, true, SEL_R, false>);
-    }
-  } else if constexpr (!PAGED) {
-    if (a.qk_mfma) {
-      if (drain) go(decode_kernel<D, G, false, SPARSE, true, 0, true>);
-      else go(decode_kernel<D, G, false, SPARSE, true, 0, false>);
-    } else {
-      if (drain) go(decode_kernel<D, G, false, SPARSE, false, 0, true>);
-      else go(decode_kernel<D, G, false, SPARSE, false, 0, false>);
-    }
-  } else if (a.qk_mfma) {
-    go(decode_kernel<D, G, PAGED, SPARSE, true, 0, false>);
+  if constexpr (PAGED) {
+    go(decode_kernel<D, G, true, SPARSE, SEL_R, false>);
+  } else if (drain) {
+    go(decode_kernel<D, G, false, SPARSE, SEL_R, true>);
   } else {
-    go(decode_kernel<D, G, PAGED, SPARSE, false, 0, false>);
+    go(decode_kernel<D, G, false, SPARSE, SEL_R, false>);
   }
   const int err = (int)hipGetLastError();
   if (err != 0 || a.max_splits <= 1) return err;

@@ -103,18 +103,6 @@ __device__ __forceinline__ f16x8 stream_load(const f16* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(p));
 }
 
-// fp32 accumulate of an 8-element fp16 dot product (v_dot2_f32_f16: exact
-// fp16 products, fp32 sums).
-__device__ __forceinline__ float dot8(f16x8 a, f16x8 b, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f16x2 x = {a[2 * i], a[2 * i + 1]};
-    f16x2 y = {b[2 * i], b[2 * i + 1]};
-    acc = __builtin_amdgcn_fdot2(x, y, acc, false);
-  }
-  return acc;
-}
-
 template <int CTRL, int ROW_MASK, int BANK_MASK>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   // lanes outside the masks, or whose source lane does not exist, read 0

@@ -42,7 +42,6 @@ struct AttnLaunch {
   const float* sel_scores;   // [B, Hkv, sel_row] page scores, or nullptr
   int32_t* sel_idx_out;      // [B, Hkv, num_sel] or nullptr
   int32_t sel_row;           // score row width (<= 16384)
-  int32_t qk_mfma;           // 1: q.k on the matrix cores, 0: v_dot2 on the VALU
 };
 
 // Split plan shared by the workspace-size query and the launch.

@@ -35,3 +35,28 @@ def test_bench_line_contract():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
     assert d["launch_floor"]["kernels"] == 2
+
+
+def test_default_line_is_the_long_context_workload():
+    """The default line: dense decode attention with the append at B=8,
+    L=131072 as value and roofline, the Quest step beside it, and the oracle
+    baseline with its parity check on sampled units."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3",
+                        "--warmup", "1", "--no-legs"],
+                       capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    assert d["config"]["workload"].startswith("long_context") and d["config"]["seq_len"] == 131072
+    rf = d["roofline"]
+    assert abs(rf["achieved"] - rf["bytes_per_call"] / (rf["us_per_call"] * 1e3)) <= 0.01 * rf["achieved"]
+    assert rf["bytes_per_call"] >= 4294967296
+    q = d["quest"]
+    assert q["us_per_step"] > 0 and q["byte_model_ratio"] == 0.09375
+    assert set(q["stages"]) == {"append_score", "select_sparse_attention"}
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["host_cores"] >= cb["cores"]
+    p = cb["parity"]
+    assert p["dense_max_abs_err"] <= 2e-3 and p["quest_max_abs_err"] <= 2e-3
+    assert p["idx_rule_violations"] == 0 and p["idx_units"] == 16

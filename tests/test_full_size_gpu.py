@@ -169,7 +169,9 @@ def test_full_quest_gqa_128k_step(da):
                                with_new=True)
     P = L // s
     meta = torch.zeros((b, hkv, P, 2, d), dtype=torch.float16, device=DEV)
-    da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"], n_new=L, page_size=s)
+    # the metadata state before the step covers keys [0, L - 1): the step's
+    # token is key L - 1
+    da.quest_meta_append(c["k"], c["v"], meta, c["seqlens"] - 1, n_new=L, page_size=s)
     units = [(0, 0), (3, 5), (7, 7), (5, 2)]
     torch.cuda.synchronize()
     k_before = {u: host(c["k"][u[0]:u[0] + 1, u[1]:u[1] + 1]) for u in units}
@@ -204,7 +206,7 @@ def test_full_quest_gqa_128k_step(da):
         # the cache now holds the appended row
         assert np.array_equal(host(c["k"][bi, kv, L - 1]), kn[0, 0])
         assert np.array_equal(host(c["v"][bi, kv, L - 1]), vn[0, 0])
-        meta_want = oquest.build_metadata(k_before[(bi, kv)], [L], s, P)
+        meta_want = oquest.build_metadata(k_before[(bi, kv)], [L - 1], s, P)
         meta_want = oquest.append_metadata(meta_want, k_u, [L], 1, s)
         _quest_unit_checks(q_u, k_u, meta_h[bi:bi + 1, kv:kv + 1],
                            scores_h[bi:bi + 1, kv:kv + 1], idx_h[bi:bi + 1, kv:kv + 1],

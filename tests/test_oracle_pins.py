@@ -382,17 +382,27 @@ def test_topk_exhaustive_tiny(seed):
 
 
 def test_topk_planted_exact_ties_pick_lower_index():
-    """Pages with identical keys score identically; the lower index wins."""
+    """Pages with identical keys score identically; the lower index wins.
+
+    Every key of pages 5, 9 and 12 is 8 * sign(w) per channel, w = the sum of
+    the group's queries, so those pages score 8 * sum_i |w_i| > 0, far above
+    any page of N(0,1) keys (whose min/max box spans about +-2): they are the
+    top three, tied, and a budget of two pages must take 5 and 9."""
     hkv, d, s = 1, 64, 16
     case = workloads.dense_case(15, 1, 4, hkv, d, 16 * s, [16 * s])
-    case.k[0, 0, 5 * s:6 * s] = case.k[0, 0, 9 * s:10 * s] = case.k[0, 0, 12 * s:13 * s] = 3.0
+    w = case.q[0].astype(np.float64).sum(0)
+    planted = np.where(w >= 0, 8.0, -8.0).astype(np.float16)
+    for p in (5, 9, 12):
+        case.k[0, 0, p * s:(p + 1) * s] = planted
     meta = oquest.build_metadata(case.k, case.seqlens, s, 16)
     u = oquest.page_scores(case.q, meta, case.seqlens, s)
     assert u[0, 0, 5] == u[0, 0, 9] == u[0, 0, 12]
-    top = np.argsort(-u[0, 0], kind="stable")[:3]
-    if set(top) == {5, 9, 12}:
-        sel = oquest.select_pages(u, case.seqlens, s, 2)[0, 0]
-        assert list(sel) == [5, 9]
+    assert u[0, 0, 5] == pytest.approx(8.0 * np.abs(w).sum(), rel=1e-12)
+    others = np.delete(u[0, 0], [5, 9, 12])
+    assert u[0, 0, 5] > others.max()
+    assert list(oquest.select_pages(u, case.seqlens, s, 2)[0, 0]) == [5, 9]
+    assert list(oquest.select_pages(u, case.seqlens, s, 1)[0, 0]) == [5]
+    assert list(oquest.select_pages(u, case.seqlens, s, 3)[0, 0]) == [5, 9, 12]
 
 
 def test_sparse_all_pages_equals_dense():

@@ -501,8 +501,9 @@ def test_sparse_over_paged_cache(da):
 def test_quest_pipeline_end_to_end(da):
     """Metadata -> score/top-K -> sparse attention, all on the GPU, against
     the oracle running the same steps from the same inputs.  The chosen pages
-    must agree under the near-tie rule; when they agree exactly, the outputs
-    must agree to the attention tolerance."""
+    must agree under the near-tie rule, and the output must match the oracle's
+    attention over the pages the GPU chose (so a legitimate near-tie swap
+    still has its output checked)."""
     page_size, budget, lens = 16, 512, [8192, 3000]
     case = workloads.dense_case(530, 2, 32, 8, 128, 8192, lens, plant_pages=8)
     meta_dev = run_meta_bulk(da, case, page_size, 512)
@@ -514,12 +515,11 @@ def test_quest_pipeline_end_to_end(da):
     meta = oquest.build_metadata(case.k, case.seqlens, page_size, 512)
     scores = oquest.page_scores(case.q, meta, case.seqlens, page_size)
     want_idx = oquest.select_pages(scores, case.seqlens, page_size, budget // page_size)
-    swaps = check_selection(host(idx), None, want_idx, scores, case.seqlens, page_size,
-                            budget // page_size)
-    if swaps == 0:
-        want = oquest.sparse_decode_attention(case.q, case.k, case.v, case.seqlens, want_idx,
-                                              page_size, case.scale)
-        assert max_err(host(out), want) <= ATOL
+    check_selection(host(idx), None, want_idx, scores, case.seqlens, page_size,
+                    budget // page_size)
+    want = oquest.sparse_decode_attention(case.q, case.k, case.v, case.seqlens, host(idx),
+                                          page_size, case.scale)
+    assert max_err(host(out), want) <= ATOL
 
 
 # ------------------------------------------------------------ q_len > 1

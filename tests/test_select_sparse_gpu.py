@@ -103,8 +103,9 @@ def test_select_without_page_idx_output(da):
 
 def test_select_sparse_parity_with_oracle(da):
     """Metadata, scores only, then the fused call, against the oracle running
-    the same steps: the choice agrees under the near-tie rule, and where it
-    agrees exactly the output is within the attention tolerance."""
+    the same steps: the choice agrees under the near-tie rule, and the output
+    is within the attention tolerance of the oracle's attention over the pages
+    the GPU chose."""
     page_size, budget, lens = 16, 512, [8192, 3000, 5]
     case = workloads.dense_case(930, 3, 32, 8, 128, 8192, lens, plant_pages=8)
     meta = run_meta_bulk(da, case, page_size, 512)
@@ -119,12 +120,11 @@ def test_select_sparse_parity_with_oracle(da):
     want_meta = oquest.build_metadata(case.k, case.seqlens, page_size, 512)
     want_scores = oquest.page_scores(case.q, want_meta, case.seqlens, page_size)
     want_idx = oquest.select_pages(want_scores, case.seqlens, page_size, budget // page_size)
-    swaps = check_selection(host(idx), host(scores).astype(np.float64), want_idx, want_scores,
-                            case.seqlens, page_size, budget // page_size)
-    if swaps == 0:
-        want = oquest.sparse_decode_attention(case.q, case.k, case.v, case.seqlens, want_idx,
-                                              page_size, case.scale)
-        assert max_err(host(out), want) <= ATOL
+    check_selection(host(idx), host(scores).astype(np.float64), want_idx, want_scores,
+                    case.seqlens, page_size, budget // page_size)
+    want = oquest.sparse_decode_attention(case.q, case.k, case.v, case.seqlens, host(idx),
+                                          page_size, case.scale)
+    assert max_err(host(out), want) <= ATOL
 
 
 def test_scores_only_mode(da):
