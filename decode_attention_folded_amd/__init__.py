@@ -9,6 +9,7 @@ the first use of an entry point loads the shared library and raises
 Entry points (same names as the C ABI):
 
 * :func:`gqa_decode_attn`          -- folded decode attention, dense or paged
+* :func:`gqa_decode_attn_noalloc`  -- the same with no workspace (library scratch)
 * :func:`gqa_decode_attn_multi`    -- the fold for q_len > 1 queries (causal alignment)
 * :func:`quest_meta_append`        -- per-page Key min/max metadata update
 * :func:`quest_page_score_topk`    -- page scores and top-K page selection
@@ -21,6 +22,7 @@ Entry points (same names as the C ABI):
 
 _EXPORTS = (
     "gqa_decode_attn",
+    "gqa_decode_attn_noalloc",
     "gqa_decode_attn_multi",
     "quest_meta_append",
     "quest_page_score_topk",

@@ -22,14 +22,17 @@ _LOCK = threading.Lock()
 DA_OK = 0
 STATUS_NAMES = {
     0: "DA_OK", -1: "DA_ERR_NULL", -2: "DA_ERR_SHAPE", -3: "DA_ERR_UNSUPPORTED",
-    -4: "DA_ERR_BUDGET", -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP",
+    -4: "DA_ERR_BUDGET", -5: "DA_ERR_WORKSPACE", -6: "DA_ERR_HIP", -7: "DA_ERR_TOO_LARGE",
 }
+
+# bytes of the library's static per-device scratch (DA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED_SYMBOLS = (
     "da_status_string", "da_workspace_size", "gqa_decode_attn", "quest_meta_append",
     "da_quest_workspace_size", "quest_page_score_topk", "quest_sparse_decode_attn",
     "gqa_repeat_kv", "quest_append_score_topk", "gqa_decode_attn_multi", "da_read_calibration",
-    "quest_select_sparse_decode_attn",
+    "quest_select_sparse_decode_attn", "gqa_decode_attn_noalloc",
 )
 
 
@@ -82,6 +85,7 @@ def load_library():
         lib.da_status_string.restype = ctypes.c_char_p
         lib.da_workspace_size.argtypes = [KVP, I32, I32, I32, SZP]
         lib.gqa_decode_attn.argtypes = [P, KVP, P, I32, F32, P, P, P, P, SZ, I32, P]
+        lib.gqa_decode_attn_noalloc.argtypes = [P, KVP, P, I32, F32, P, P, P, I32, P]
         lib.quest_meta_append.argtypes = [KVP, P, I32, P, I32, P, P, P]
         lib.da_quest_workspace_size.argtypes = [I32, I32, I32, SZP]
         lib.quest_page_score_topk.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, P, P,
@@ -265,6 +269,36 @@ def gqa_decode_attn(q, k_cache, v_cache, seqlens, *, scale=None, k_new=None, v_n
                                _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(ws), ws.numel(),
                                num_splits, _stream_handle(q.device, stream)),
            "gqa_decode_attn")
+    return out
+
+
+def gqa_decode_attn_noalloc(q, k_cache, v_cache, seqlens, out, *, scale=None, k_new=None,
+                            v_new=None, page_table=None, page_size=0, num_splits=0, stream=None):
+    """gqa_decode_attn without a workspace (see ``gqa_decode_attn_noalloc`` in
+    decode_attn.h): the library call allocates nothing, its split partials
+    live in the library's static per-device scratch.  ``out`` [B, Hq, D] fp16
+    must be given (nothing is allocated here either).  Calls that may overlap
+    on one GPU race on that scratch.  Returns ``out``."""
+    lib = load_library()
+    _need(q, "q", torch.float16, 3)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    batch, hq, d = q.shape
+    desc = _kv_desc(k_cache, v_cache, batch, page_table, page_size)
+    _check_common(q, seqlens, desc)
+    if k_new is not None or v_new is not None:
+        _need(k_new, "k_new", torch.float16, 3)
+        _need(v_new, "v_new", torch.float16, 3)
+        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+            if tuple(t.shape) != (batch, desc.num_kv_heads, d):
+                raise ValueError(f"{name} must be [B, Hkv, D]")
+    _need(out, "out", torch.float16, 3)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape [B, Hq, D]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.gqa_decode_attn_noalloc(_ptr(q), ctypes.byref(desc), _ptr(seqlens), hq, scale,
+                                       _ptr(k_new), _ptr(v_new), _ptr(out), num_splits,
+                                       _stream_handle(q.device, stream)),
+           "gqa_decode_attn_noalloc")
     return out
 
 

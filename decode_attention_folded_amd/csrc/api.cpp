@@ -138,11 +138,16 @@ struct PageSelect {
   int32_t* idx_out;     // [B, Hkv, K] the choice, or nullptr
 };
 
+// Where the split partials go: the caller's workspace, or (kLibraryScratch)
+// the library's static device scratch, whose address is fetched only after
+// every argument check has passed.
+enum WsSource { kCallerWorkspace, kLibraryScratch };
+
 int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
                   const int32_t* page_idx, int32_t budget_tokens, int32_t num_rows,
                   int32_t q_len, float scale, const void* k_new, const void* v_new, void* out,
                   void* workspace, size_t workspace_bytes, int32_t num_splits, void* stream,
-                  const PageSelect* select = nullptr) {
+                  const PageSelect* select = nullptr, WsSource ws_source = kCallerWorkspace) {
   Shape s;
   int st = check_cache(kv, num_rows, &s);
   if (st != DA_OK) return st;
@@ -166,6 +171,11 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
   // one workgroup per (split, b, kv) on a 1-D grid
   if ((int64_t)plan.max_splits * s.batch * s.hkv > INT32_MAX) return DA_ERR_SHAPE;
   const WsLayout w = ws_layout(s, plan);
+  if (ws_source == kLibraryScratch) {
+    if (w.total > da::noalloc_scratch_bytes()) return DA_ERR_TOO_LARGE;
+    if (da::noalloc_scratch(&workspace) != 0) return DA_ERR_HIP;
+    workspace_bytes = da::noalloc_scratch_bytes();
+  }
   if (workspace == nullptr) return DA_ERR_NULL;
   if (!aligned16(workspace)) return DA_ERR_SHAPE;
   if (workspace_bytes < w.total) return DA_ERR_WORKSPACE;
@@ -216,6 +226,9 @@ const char* da_status_string(int status) {
     case DA_ERR_BUDGET: return "DA_ERR_BUDGET: token budget must be a positive multiple of the page size";
     case DA_ERR_WORKSPACE: return "DA_ERR_WORKSPACE: workspace too small";
     case DA_ERR_HIP: return "DA_ERR_HIP: HIP launch or runtime error";
+    case DA_ERR_TOO_LARGE:
+      return "DA_ERR_TOO_LARGE: the call needs more split-partial scratch than the library's "
+             "static buffer holds (DA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -245,6 +258,13 @@ int gqa_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens
                     void* stream) {
   return run_attention(q, kv, seqlens, nullptr, 0, num_q_heads, 1, scale, k_new, v_new, out,
                        workspace, workspace_bytes, num_splits, stream);
+}
+
+int gqa_decode_attn_noalloc(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
+                            int32_t num_q_heads, float scale, const void* k_new,
+                            const void* v_new, void* out, int32_t num_splits, void* stream) {
+  return run_attention(q, kv, seqlens, nullptr, 0, num_q_heads, 1, scale, k_new, v_new, out,
+                       nullptr, 0, num_splits, stream, nullptr, kLibraryScratch);
 }
 
 int gqa_decode_attn_multi(const void* q, const da_kv_cache* kv, const int32_t* seqlens,

@@ -117,6 +117,12 @@ struct RepeatLaunch {
 int launch_repeat_kv(const RepeatLaunch& p, void* stream);
 int repeat_kv_rows_per_workgroup();
 
+// The library's static scratch for the entry point that allocates nothing:
+// its size, and its device address on the current device (looked up once per
+// device; 0 or a HIP error code).
+size_t noalloc_scratch_bytes();
+int noalloc_scratch(void** ptr);
+
 // Streaming-read calibration over `bytes` (a multiple of 16) at `src`.
 int launch_read_calibration(const void* src, uint64_t bytes, uint32_t* sink, void* stream);
 

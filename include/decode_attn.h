@@ -49,8 +49,14 @@ enum da_status {
   DA_ERR_UNSUPPORTED = -3, /* D not in {64,128}, G not in {1,2,4,8}, S not in {8,16,32,64} */
   DA_ERR_BUDGET = -4,      /* token budget not a positive multiple of S          */
   DA_ERR_WORKSPACE = -5,   /* workspace too small                                */
-  DA_ERR_HIP = -6          /* a HIP launch or query failed (e.g. no device)      */
+  DA_ERR_HIP = -6,         /* a HIP launch or query failed (e.g. no device)      */
+  DA_ERR_TOO_LARGE = -7    /* gqa_decode_attn_noalloc: the call needs more than
+                              DA_NOALLOC_SCRATCH_BYTES of split partials        */
 };
+
+/* Size of the library's static per-device scratch used by
+ * gqa_decode_attn_noalloc (32 MiB). */
+#define DA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /*
  * A KV cache, described on the host (the struct itself is host memory).
@@ -119,6 +125,29 @@ int gqa_decode_attn(const void* q, const da_kv_cache* kv, const int32_t* seqlens
                     int32_t num_q_heads, float scale, const void* k_new, const void* v_new,
                     void* out, void* workspace, size_t workspace_bytes, int32_t num_splits,
                     void* stream);
+
+/*
+ * gqa_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and result as gqa_decode_attn, without the workspace: the
+ * split partials go to a static device array inside the library
+ * (DA_NOALLOC_SCRATCH_BYTES per GPU, held by every GPU the library runs on
+ * until the process ends).  The call allocates and frees nothing; the caller
+ * still passes every input and output buffer.
+ *
+ *   arguments as gqa_decode_attn (workspace omitted).
+ *   Returns DA_ERR_TOO_LARGE, before anything is enqueued, when
+ *   da_workspace_size(kv, num_q_heads, 0, num_splits) exceeds
+ *   DA_NOALLOC_SCRATCH_BYTES; otherwise as gqa_decode_attn.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (different streams, concurrent host threads) race on it and must be
+ * ordered by the caller.  The scratch needs no clearing between calls (each
+ * call writes every partial it reads).  Its device address is looked up on
+ * the first call on each device (the device current at the call).
+ */
+int gqa_decode_attn_noalloc(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
+                            int32_t num_q_heads, float scale, const void* k_new,
+                            const void* v_new, void* out, int32_t num_splits, void* stream);
 
 /*
  * Folded GQA attention for q_len > 1 query positions per head (chunked

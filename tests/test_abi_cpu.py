@@ -101,7 +101,7 @@ def test_select_sparse_validation_codes(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         s = lib.da_status_string(code).decode()
         assert s.startswith("DA_")
     assert lib.da_status_string(-99) == b"unknown status"
@@ -279,3 +279,32 @@ def test_workspace_follows_the_split_plan(lib, fields, hq, budget, splits, page_
     out = ctypes.c_size_t()
     assert lib.da_workspace_size(ctypes.byref(desc), hq, budget, splits, ctypes.byref(out)) == 0
     assert out.value == _plan_bytes(units, want_splits, hq // desc.num_kv_heads, desc.head_dim)
+
+
+def _noalloc(lib, desc, hq=32, q=FAKE, seqlens=FAKE, out=FAKE, splits=0):
+    P = ctypes.c_void_p
+    return lib.gqa_decode_attn_noalloc(P(q), ctypes.byref(desc), P(seqlens), hq, 0.125, None,
+                                       None, P(out), splits, None)
+
+
+def test_noalloc_validation_codes(lib):
+    """The entry point without a workspace checks its arguments, then the size
+    of its split partials against the library's static scratch, before any
+    HIP call."""
+    assert _noalloc(lib, _desc(), q=0) == -1
+    assert _noalloc(lib, _desc(), out=0) == -1
+    assert _noalloc(lib, _desc(), hq=30) == -2
+    assert _noalloc(lib, _desc(batch=0), q=0, out=0) == 0
+    # 64 sequences x 8 KV heads x 2^20 keys: 256 splits of fp32 partials per
+    # unit, far beyond 32 MiB
+    huge = _desc(batch=64, capacity=1 << 20)
+    size = ctypes.c_size_t()
+    assert lib.da_workspace_size(ctypes.byref(huge), 32, 0, 0, ctypes.byref(size)) == 0
+    assert size.value > (32 << 20)
+    assert _noalloc(lib, huge) == -7
+    assert b"DA_ERR_TOO_LARGE" in lib.da_status_string(-7)
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_noalloc_without_a_device_reports_hip_error(lib):
+    assert _noalloc(lib, _desc(batch=1)) == -6
