@@ -248,6 +248,8 @@ int da_workspace_size(const da_kv_cache* kv, int32_t num_q_heads, int32_t budget
   }
   const da::SplitPlan plan = plan_splits(s, max_stream_keys(s, budget_tokens), num_splits,
                                          s.paged || budget_tokens > 0);
+  // the same grid limit as the calls: one workgroup per (split, b, kv)
+  if ((int64_t)plan.max_splits * s.batch * s.hkv > INT32_MAX) return DA_ERR_SHAPE;
   *bytes_out = ws_layout(s, plan).total;
   return DA_OK;
 }

@@ -213,11 +213,18 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
 // DRAIN (contiguous cache, chunks of at most two ring rounds per wave): the
 // ring's last round issues no loads past the chunk.  The arithmetic is the
 // same as without it, so both variants give bitwise equal results.
+//
+// attend_chunk runs chunk `split_u` of unit `unit_u` (unit = b * Hkv + kv)
+// with the calling workgroup: it writes the unit's output when the unit has
+// one split with keys, a partial when it has more and split_u is below that
+// count, and nothing otherwise (split 0 of a unit without keys writes the
+// zero output).
 template <int D, int G, bool PAGED, bool SPARSE, int SEL_R, bool DRAIN>
-__global__ void __launch_bounds__(kThreads)
-    decode_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
-                  void* v, const void* __restrict__ list, int batch, int hkv, int list_width,
-                  int chunk_geom, AttnLaunch a) {
+__device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens,
+                                             const void* __restrict__ q, void* k, void* v,
+                                             const void* __restrict__ list, int batch, int hkv,
+                                             int list_width, int chunk_geom, const AttnLaunch& a,
+                                             uint32_t split_u, uint32_t unit_u) {
   constexpr bool SELECT = SEL_R > 0;
   static_assert(!SELECT || SPARSE, "page selection feeds the selected-page stream");
   static_assert(!DRAIN || !PAGED, "the draining ring is built for contiguous caches");
@@ -241,10 +248,6 @@ __global__ void __launch_bounds__(kThreads)
   const int rv = lane & 7;         // V key slots rv, rv + 8
   const int cv = lane >> 3;        // V chunk group (0..7)
   const bool upper = (lane & 8) != 0;
-  // grid < 2^31 workgroups (checked on the host): 32-bit index arithmetic
-  const uint32_t n_units = (uint32_t)batch * (uint32_t)hkv;
-  const uint32_t split_u = blockIdx.x / n_units;
-  const uint32_t unit_u = blockIdx.x - split_u * n_units;
   const uint32_t b_u = unit_u / (uint32_t)hkv;
   const int split = (int)split_u;
   const int64_t unit = unit_u;
@@ -670,6 +673,20 @@ __global__ void __launch_bounds__(kThreads)
       }
     }
   }
+}
+
+// One workgroup per (split, unit) of a 1-D grid, unit index fastest.
+template <int D, int G, bool PAGED, bool SPARSE, int SEL_R, bool DRAIN>
+__global__ void __launch_bounds__(kThreads)
+    decode_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
+                  void* v, const void* __restrict__ list, int batch, int hkv, int list_width,
+                  int chunk_geom, AttnLaunch a) {
+  // grid < 2^31 workgroups (checked on the host): 32-bit index arithmetic
+  const uint32_t n_units = (uint32_t)batch * (uint32_t)hkv;
+  const uint32_t split_u = blockIdx.x / n_units;
+  const uint32_t unit_u = blockIdx.x - split_u * n_units;
+  attend_chunk<D, G, PAGED, SPARSE, SEL_R, DRAIN>(seqlens, q, k, v, list, batch, hkv,
+                                                  list_width, chunk_geom, a, split_u, unit_u);
 }
 
 // Merge kernel: one workgroup per (b, kv) unit, one thread per output element

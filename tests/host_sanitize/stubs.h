@@ -1,0 +1,20 @@
+// The launch records of the host-only stub launchers (stub_launchers.cpp).
+#pragma once
+
+#include "../../decode_attention_folded_amd/csrc/kernels.h"
+
+namespace da {
+
+struct StubRecord {
+  enum Kind { kNone, kAttn, kMeta, kScore, kRepeat, kCalibration };
+  Kind last = kNone;
+  long launches = 0;
+  AttnLaunch attn{};
+  MetaLaunch meta{};
+  ScoreLaunch score{};
+  RepeatLaunch repeat{};
+};
+
+extern StubRecord g_stub;
+
+}  // namespace da
