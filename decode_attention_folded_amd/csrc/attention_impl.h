@@ -675,16 +675,87 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
   }
 }
 
-// One workgroup per (split, unit) of a 1-D grid, unit index fastest.
+// Flat work list of a dense stream over sequences of unequal lengths: chunk
+// `w` of the grid (any workgroup, each wave computes the same answer) in an
+// order that holds only chunks with keys -- a sequence without keys keeps one
+// chunk, which writes its zero output -- longest sequences first (equal
+// lengths in index order) when there are at most 64 sequences, in index order
+// otherwise.  Consecutive workgroups take the Hkv heads of one chunk, so the
+// heads of every chunk spread over the XCDs.  Returns false past the last
+// chunk.  (The grid, max_splits * B * Hkv workgroups, is sized on the host,
+// which does not know the lengths.)
+__device__ __forceinline__ bool flat_chunk(const int32_t* __restrict__ seqlens, int batch, int hkv,
+                                           int tiles_per_split, int capacity, uint32_t w,
+                                           uint32_t& split_u, uint32_t& unit_u) {
+  const int lane = lane_in_wave();
+  const uint32_t f = w / (uint32_t)hkv;  // flat chunk index
+  const uint32_t kv = w - f * (uint32_t)hkv;
+  auto chunks = [&](int L) {
+    L = L < 0 ? 0 : (L > capacity ? capacity : L);
+    const int n = ((L + kTileKeys - 1) / kTileKeys + tiles_per_split - 1) / tiles_per_split;
+    return n < 1 ? 1 : n;
+  };
+  if (batch <= kWave) {
+    int L = lane < batch ? seqlens[lane] : -1;
+    L = lane < batch ? (L < 0 ? 0 : (L > capacity ? capacity : L)) : -1;
+    const int n = lane < batch ? chunks(L) : 0;
+    int rank = 0;  // sequences before this one: longer, or as long with a lower index
+    for (int j = 0; j < batch; ++j) {
+      const int Lj = __builtin_amdgcn_readlane(L, j);
+      rank += (Lj > L || (Lj == L && j < lane)) ? 1 : 0;
+    }
+    int start = 0;  // its first flat chunk: the chunks of every sequence before it
+    for (int j = 0; j < batch; ++j) {
+      const int rj = __builtin_amdgcn_readlane(rank, j);
+      const int nj = __builtin_amdgcn_readlane(n, j);
+      start += rj < rank ? nj : 0;
+    }
+    const uint64_t hit =
+        __ballot(lane < batch && (uint32_t)start <= f && f < (uint32_t)(start + n));
+    if (hit == 0) return false;
+    const int b = __builtin_ctzll(hit);
+    split_u = f - (uint32_t)__builtin_amdgcn_readlane(start, b);
+    unit_u = (uint32_t)b * (uint32_t)hkv + kv;
+    return true;
+  }
+  uint32_t base = 0;
+  for (int b0 = 0; b0 < batch; b0 += kWave) {
+    const int b = b0 + lane;
+    const uint32_t n = b < batch ? (uint32_t)chunks(seqlens[b]) : 0u;
+    const uint32_t inc = wave_inclusive_scan(n);
+    const uint32_t start = base + inc - n;
+    const uint64_t hit = __ballot(b < batch && start <= f && f < start + n);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      split_u = f - (uint32_t)__builtin_amdgcn_readlane((int)start, l);
+      unit_u = (uint32_t)(b0 + l) * (uint32_t)hkv + kv;
+      return true;
+    }
+    base += (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+  }
+  return false;
+}
+
+// One workgroup per (split, unit).  The paged dense stream (the batched
+// decode of sequences of unequal lengths) takes its chunk from the flat work
+// list; the other streams use a 1-D grid of splits x units, unit index
+// fastest.
 template <int D, int G, bool PAGED, bool SPARSE, int SEL_R, bool DRAIN>
 __global__ void __launch_bounds__(kThreads)
     decode_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
                   void* v, const void* __restrict__ list, int batch, int hkv, int list_width,
                   int chunk_geom, AttnLaunch a) {
-  // grid < 2^31 workgroups (checked on the host): 32-bit index arithmetic
-  const uint32_t n_units = (uint32_t)batch * (uint32_t)hkv;
-  const uint32_t split_u = blockIdx.x / n_units;
-  const uint32_t unit_u = blockIdx.x - split_u * n_units;
+  uint32_t split_u, unit_u;
+  if constexpr (PAGED && !SPARSE) {
+    if (!flat_chunk(seqlens, batch, hkv, chunk_geom & 0xFFFF, a.capacity, blockIdx.x, split_u,
+                    unit_u))
+      return;
+  } else {
+    // grid < 2^31 workgroups (checked on the host): 32-bit index arithmetic
+    const uint32_t n_units = (uint32_t)batch * (uint32_t)hkv;
+    split_u = blockIdx.x / n_units;
+    unit_u = blockIdx.x - split_u * n_units;
+  }
   attend_chunk<D, G, PAGED, SPARSE, SEL_R, DRAIN>(seqlens, q, k, v, list, batch, hkv,
                                                   list_width, chunk_geom, a, split_u, unit_u);
 }
