@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
 * :func:`quest_select_sparse_decode_attn` -- top-K fused into that attention
 * :func:`gqa_repeat_kv`            -- the materialised repeat_kv copy (A/B baseline)
 * :func:`read_calibration`         -- streaming-read calibration (measurement helper)
+* :func:`check_cache`              -- reports lengths and page-table entries the calls
+                                      would clamp or mask (debugging aid)
 """
 
 _EXPORTS = (
@@ -31,6 +33,7 @@ _EXPORTS = (
     "quest_select_sparse_decode_attn",
     "gqa_repeat_kv",
     "read_calibration",
+    "check_cache",
     "workspace_bytes",
     "quest_workspace_bytes",
     "Workspace",

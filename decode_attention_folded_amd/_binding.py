@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "da_status_string", "da_workspace_size", "gqa_decode_attn", "quest_meta_append",
     "da_quest_workspace_size", "quest_page_score_topk", "quest_sparse_decode_attn",
     "gqa_repeat_kv", "quest_append_score_topk", "gqa_decode_attn_multi", "da_read_calibration",
-    "quest_select_sparse_decode_attn", "gqa_decode_attn_noalloc",
+    "quest_select_sparse_decode_attn", "gqa_decode_attn_noalloc", "da_check_cache",
 )
 
 
@@ -96,6 +96,7 @@ def load_library():
         lib.quest_append_score_topk.argtypes = [P, KVP, P, I32, P, I32, I32, P, P, P, P, P, SZ,
                                                 P]
         lib.da_read_calibration.argtypes = [P, SZ, P, P]
+        lib.da_check_cache.argtypes = [KVP, P, P, P]
         lib.quest_select_sparse_decode_attn.argtypes = [P, KVP, P, P, I32, I32, I32, F32, P, P,
                                                         P, SZ, I32, P]
         for name in EXPORTED_SYMBOLS[1:]:
@@ -554,3 +555,22 @@ def quest_select_sparse_decode_attn(q, k_cache, v_cache, seqlens, page_scores, *
                                                _stream_handle(q.device, stream)),
            "quest_select_sparse_decode_attn")
     return out
+
+
+def check_cache(k_cache, v_cache, seqlens, *, page_table=None, page_size=0, report=None,
+                stream=None):
+    """Device-side precondition check (see ``da_check_cache`` in decode_attn.h):
+    returns report [4] int32 on the device -- sequences with a length outside
+    [0, capacity], page-table entries of valid pages outside the pool, the
+    lowest offending sequence index (-1 if none), 0."""
+    lib = load_library()
+    _need(seqlens, "seqlens", torch.int32, 1)
+    desc = _kv_desc(k_cache, v_cache, seqlens.shape[0], page_table, page_size)
+    if report is None:
+        report = torch.zeros(4, dtype=torch.int32, device=seqlens.device)
+    _need(report, "report", torch.int32, 1)
+    if report.numel() < 4:
+        raise ValueError("report must hold 4 int32")
+    _check(lib.da_check_cache(ctypes.byref(desc), _ptr(seqlens), _ptr(report),
+                              _stream_handle(seqlens.device, stream)), "da_check_cache")
+    return report

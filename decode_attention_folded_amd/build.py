@@ -18,7 +18,7 @@ LIB_NAME = "libdecode_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 HIP_SOURCES = ["decode_kernel.hip", "decode_select.hip", "quest_kernels.hip", "repeat_kv.hip",
-               "calibrate.hip", "noalloc.hip"]
+               "calibrate.hip", "noalloc.hip", "check.hip"]
 HOST_SOURCES = ["api.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code.  The kernels'

@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include "../../include/decode_attn.h"
+#include "check.h"
 #include "kernels.h"
 
 namespace {
@@ -507,6 +508,26 @@ int quest_select_sparse_decode_attn(const void* q, const da_kv_cache* kv,
   sel.idx_out = page_idx;
   return run_attention(q, kv, seqlens, nullptr, budget_tokens, num_q_heads, 1, scale, nullptr,
                        nullptr, out, workspace, workspace_bytes, num_splits, stream, &sel);
+}
+
+int da_check_cache(const da_kv_cache* kv, const int32_t* seqlens, int32_t* report,
+                   void* stream) {
+  Shape s;
+  // the group size does not matter here; pass Hq = Hkv
+  const int st = check_cache(kv, kv != nullptr ? kv->num_kv_heads : 1, &s);
+  if (st != DA_OK) return st;
+  if (s.batch == 0) return DA_OK;  // nothing to check
+  if (seqlens == nullptr || report == nullptr) return DA_ERR_NULL;
+  da::CheckLaunch a;
+  a.seqlens = seqlens;
+  a.page_table = kv->page_table;
+  a.report = report;
+  a.batch = s.batch;
+  a.capacity = s.capacity;
+  a.page_shift = s.paged ? log2i(s.page_size) : 0;
+  a.max_pages = s.max_pages;
+  a.num_pages = kv->num_pages;
+  return da::launch_check(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
 }
 
 int da_read_calibration(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

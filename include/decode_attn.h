@@ -332,6 +332,30 @@ int quest_select_sparse_decode_attn(const void* q, const da_kv_cache* kv,
                                     int32_t num_splits, void* stream);
 
 /*
+ * Debugging aid, not part of the method: reports the device-side inputs that
+ * the other calls clamp or mask silently instead of failing on (they cannot
+ * see device memory at call time).  Run it on the same cache and lengths,
+ * on the same stream, when results look wrong.
+ *
+ *   kv         (host)   cache description (contiguous or paged)
+ *   seqlens    (device) int32 [B]
+ *   report     (device) int32 [4] out, written by one small kernel:
+ *              [0] sequences with L_b < 0 or L_b > capacity (they are clamped
+ *                  to [0, capacity] by every call);
+ *              [1] paged caches: page-table entries of pages that hold a
+ *                  valid token (p < ceil(min(L_b, capacity) / S)) that lie
+ *                  outside [0, num_pages) (every call masks those tokens);
+ *                  0 for a contiguous cache;
+ *              [2] the lowest sequence index with such an input, or -1;
+ *              [3] 0.
+ * Asynchronous on `stream`; reads seqlens and the page table only.
+ * Returns DA_OK (and writes nothing) for B = 0, DA_ERR_NULL / DA_ERR_SHAPE /
+ * DA_ERR_UNSUPPORTED for bad arguments as the attention calls check them,
+ * or DA_ERR_HIP.
+ */
+int da_check_cache(const da_kv_cache* kv, const int32_t* seqlens, int32_t* report, void* stream);
+
+/*
  * Measurement helper, not part of the method: the HBM read rate a plain
  * streaming kernel reaches, the practical ceiling next to the nominal peak
  * for kernels that stream K/V or page metadata.  Reads the `bytes` bytes at

@@ -286,6 +286,24 @@ void sparse_checks() {
                 DA_ERR_UNSUPPORTED);
 }
 
+void check_checks() {
+  da_kv_cache kv = contiguous();
+  int32_t* report = fake_i(17);
+  EXPECT_STATUS(da_check_cache(&kv, fake_i(7), report, nullptr), DA_OK);
+  CHECK(da::g_stub.last == da::StubRecord::kCheck);
+  EXPECT_STATUS(da_check_cache(&kv, nullptr, report, nullptr), DA_ERR_NULL);
+  EXPECT_STATUS(da_check_cache(&kv, fake_i(7), nullptr, nullptr), DA_ERR_NULL);
+  EXPECT_STATUS(da_check_cache(nullptr, fake_i(7), report, nullptr), DA_ERR_NULL);
+  da_kv_cache pk = paged();
+  EXPECT_STATUS(da_check_cache(&pk, fake_i(7), report, nullptr), DA_OK);
+  da_kv_cache bad = paged();
+  bad.page_size = 24;
+  EXPECT_STATUS(da_check_cache(&bad, fake_i(7), report, nullptr), DA_ERR_UNSUPPORTED);
+  da_kv_cache empty = kv;
+  empty.batch = 0;
+  EXPECT_STATUS(da_check_cache(&empty, nullptr, nullptr, nullptr), DA_OK);
+}
+
 void calibration_checks() {
   uint32_t* sink = static_cast<uint32_t*>(fake(15));
   EXPECT_STATUS(da_read_calibration(fake(16), 1 << 20, sink, nullptr), DA_OK);
@@ -343,6 +361,7 @@ void fuzz(uint64_t seed, int rounds) {
     (void)gqa_decode_attn_multi(fake(4), &kv, fake_i(7), hq, 1 + (int)(rng() % 9), 0.1f,
                                 fake(5), fake(6), kBigWs, splits, nullptr);
     (void)gqa_repeat_kv(&kv, hq, fake_i(7), fake(8), fake(9), nullptr);
+    (void)da_check_cache(&kv, fake_i(7), fake_i(17), nullptr);
     (void)quest_meta_append(&kv, fake(10), mp, fake_i(7), pick(rng, kInts, n_ints), nullptr,
                             nullptr, nullptr);
     (void)quest_meta_append(&kv, fake(10), mp, fake_i(7), 1, fake(11), fake(12), nullptr);
@@ -394,6 +413,7 @@ int main(int argc, char** argv) {
   meta_checks();
   score_checks();
   sparse_checks();
+  check_checks();
   calibration_checks();
   fuzz(20261202, rounds);
   print_sizes();

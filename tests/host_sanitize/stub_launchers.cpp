@@ -49,6 +49,11 @@ int launch_repeat_kv(const RepeatLaunch& p, void*) {
   return 0;
 }
 int repeat_kv_rows_per_workgroup() { return 64; }
+int launch_check(const CheckLaunch&, void*) {
+  g_stub.last = StubRecord::kCheck;
+  ++g_stub.launches;
+  return 0;
+}
 int launch_read_calibration(const void*, uint64_t, uint32_t*, void*) {
   g_stub.last = StubRecord::kCalibration;
   ++g_stub.launches;

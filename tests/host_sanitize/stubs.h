@@ -1,12 +1,13 @@
 // The launch records of the host-only stub launchers (stub_launchers.cpp).
 #pragma once
 
+#include "../../decode_attention_folded_amd/csrc/check.h"
 #include "../../decode_attention_folded_amd/csrc/kernels.h"
 
 namespace da {
 
 struct StubRecord {
-  enum Kind { kNone, kAttn, kMeta, kScore, kRepeat, kCalibration };
+  enum Kind { kNone, kAttn, kMeta, kScore, kRepeat, kCheck, kCalibration };
   Kind last = kNone;
   long launches = 0;
   AttnLaunch attn{};
