@@ -99,17 +99,22 @@ da::SplitPlan plan_splits(const Shape& s, int max_keys, int num_splits, bool pag
 }
 
 struct WsLayout {
-  size_t ml, o, total;
+  size_t ml, o, idx, total;
 };
 
 // Workspace: per (b, kv, split) partial softmax state (m, l) and
-// unnormalised output o, all fp32.
-WsLayout ws_layout(const Shape& s, const da::SplitPlan& p) {
+// unnormalised output o, all fp32; for the selected-page stream (k_sel > 0
+// chosen pages per unit) also room for the choice [B, Hkv, k_sel] int32,
+// which the page-selecting call fills when the unit has more pages than the
+// attention launch selects itself and the caller keeps no copy.
+WsLayout ws_layout(const Shape& s, const da::SplitPlan& p, int k_sel) {
   const size_t units = (size_t)s.batch * s.hkv;
   WsLayout w;
   w.ml = 0;
   w.o = w.ml + align256(units * p.max_splits * s.group * 2 * sizeof(float));
-  w.total = w.o + units * p.max_splits * s.group * s.d * sizeof(float);
+  const size_t o_bytes = units * p.max_splits * s.group * s.d * sizeof(float);
+  w.idx = w.o + align256(o_bytes);
+  w.total = k_sel > 0 ? w.idx + units * (size_t)k_sel * sizeof(int32_t) : w.o + o_bytes;
   if (w.total == 0) w.total = 256;
   return w;
 }
@@ -171,7 +176,8 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
                                          num_splits, s.paged || sparse);
   // one workgroup per (split, b, kv) on a 1-D grid
   if ((int64_t)plan.max_splits * s.batch * s.hkv > INT32_MAX) return DA_ERR_SHAPE;
-  const WsLayout w = ws_layout(s, plan);
+  const int k_sel = sparse ? budget_tokens / s.page_size : 0;
+  const WsLayout w = ws_layout(s, plan, k_sel);
   if (ws_source == kLibraryScratch) {
     if (w.total > da::noalloc_scratch_bytes()) return DA_ERR_TOO_LARGE;
     if (da::noalloc_scratch(&workspace) != 0) return DA_ERR_HIP;
@@ -204,13 +210,37 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
   a.page_shift = (s.paged || sparse) ? log2i(s.page_size) : 0;
   a.max_pages = s.max_pages;
   a.num_pages = kv->num_pages;
-  a.num_sel = sparse ? budget_tokens / s.page_size : 0;
+  a.num_sel = k_sel;
   a.sel_scores = select != nullptr ? select->scores : nullptr;
   a.sel_row = select != nullptr ? select->row : 0;
   a.sel_idx_out = select != nullptr ? select->idx_out : nullptr;
   a.tiles_per_split = plan.tiles_per_split;
   a.max_splits = plan.max_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
+  if (select != nullptr && select->row > da::topk_max_pages()) {
+    // More pages per unit than the attention launch selects itself: the
+    // streaming top-K writes the choice (to page_idx, else the workspace),
+    // then the attention reads it as a given list.
+    if (s.batch > kMaxGridDim || s.hkv > kMaxGridDim) return DA_ERR_SHAPE;  // its (Hkv, B) grid
+    int32_t* idx = select->idx_out != nullptr ? select->idx_out
+                                              : reinterpret_cast<int32_t*>(ws + w.idx);
+    da::ScoreLaunch t{};
+    t.seqlens = seqlens;
+    t.scores = const_cast<float*>(select->scores);
+    t.page_idx = idx;
+    t.batch = s.batch;
+    t.num_kv_heads = s.hkv;
+    t.group = s.group;
+    t.head_dim = s.d;
+    t.page_shift = log2i(s.page_size);
+    t.meta_max_pages = select->row;
+    t.num_sel = k_sel;
+    if (da::launch_topk_only(t, stream) != 0) return DA_ERR_HIP;
+    a.page_idx = idx;
+    a.sel_scores = nullptr;
+    a.sel_row = 0;
+    a.sel_idx_out = nullptr;
+  }
   return da::launch_decode(a, stream) == 0 ? DA_OK : DA_ERR_HIP;
 }
 
@@ -251,7 +281,7 @@ int da_workspace_size(const da_kv_cache* kv, int32_t num_q_heads, int32_t budget
                                          s.paged || budget_tokens > 0);
   // the same grid limit as the calls: one workgroup per (split, b, kv)
   if ((int64_t)plan.max_splits * s.batch * s.hkv > INT32_MAX) return DA_ERR_SHAPE;
-  *bytes_out = ws_layout(s, plan).total;
+  *bytes_out = ws_layout(s, plan, budget_tokens > 0 ? budget_tokens / s.page_size : 0).total;
   return DA_OK;
 }
 
@@ -393,7 +423,6 @@ int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_page
   if (head_dim != 64 && head_dim != 128) return DA_ERR_UNSUPPORTED;
   if (!is_pow2_in(page_size, 8, 64)) return DA_ERR_UNSUPPORTED;
   if (budget_tokens <= 0 || budget_tokens % page_size != 0) return DA_ERR_BUDGET;
-  if (meta_max_pages > da::topk_max_pages()) return DA_ERR_UNSUPPORTED;
   if (batch == 0) return DA_OK;  // nothing to read or write
   if (q == nullptr || meta == nullptr || seqlens == nullptr) return DA_ERR_NULL;
   if (page_idx == nullptr && page_scores == nullptr) return DA_ERR_NULL;  // nothing to output
@@ -444,7 +473,6 @@ int quest_append_score_topk(const void* q, const da_kv_cache* kv, void* meta,
   if (budget_tokens <= 0 || budget_tokens % s.page_size != 0) return DA_ERR_BUDGET;
   if (meta_max_pages < 1 || (int64_t)meta_max_pages * s.page_size < s.capacity)
     return DA_ERR_SHAPE;
-  if (meta_max_pages > da::topk_max_pages()) return DA_ERR_UNSUPPORTED;
   if (s.batch == 0) return DA_OK;  // nothing to read or write
   if (q == nullptr || meta == nullptr || seqlens == nullptr || k_new == nullptr ||
       v_new == nullptr || kv->k == nullptr || kv->v == nullptr)
@@ -500,7 +528,6 @@ int quest_select_sparse_decode_attn(const void* q, const da_kv_cache* kv,
   if (st != DA_OK) return st;
   if (meta_max_pages < 1 || (int64_t)meta_max_pages * s.page_size < s.capacity)
     return DA_ERR_SHAPE;  // every page that can hold a valid token has a score
-  if (meta_max_pages > da::topk_max_pages()) return DA_ERR_UNSUPPORTED;
   if (s.batch > 0 && page_scores == nullptr) return DA_ERR_NULL;
   PageSelect sel;
   sel.scores = page_scores;

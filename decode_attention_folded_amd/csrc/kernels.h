@@ -98,6 +98,10 @@ struct ScoreLaunch {
   int64_t num_pages;
 };
 int launch_score_topk(const ScoreLaunch& p, void* stream);
+// The top-K alone over p.scores (p.page_idx receives it), for any page count.
+int launch_topk_only(const ScoreLaunch& p, void* stream);
+// Pages per unit up to which the top-K holds the scores in registers (and the
+// attention launch can select its own pages); above it the streaming select runs.
 int topk_max_pages();
 
 // Materialised repeat_kv: rows t < L_b of every KV head copied to its G query

@@ -28,6 +28,10 @@
 //                       is deterministic.  (Bit-serial passes without atomics
 //                       measured slower: 7-8 barrier-bound passes cost more
 //                       than 2-3 histogram passes.)
+//   topk_stream_kernel  the same choice for units with more than 16,384 pages:
+//                       1,024 threads, radix passes that re-read the score row
+//                       instead of holding it, and output positions from a
+//                       block scan over contiguous runs of pages.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -297,6 +301,190 @@ __global__ void __launch_bounds__(kTopkThreads)
   select_top_k<R>(raw, n_pages, K, emit);
 }
 
+// ------------------------------------------------------------ streaming top-K
+
+constexpr int kStreamTopkThreads = 1024;
+constexpr int kStreamTopkWaves = kStreamTopkThreads / kWave;
+constexpr int kStreamUnroll = 8;  // score loads in flight per thread
+
+// key >> shift for shift in [0, 32]
+__device__ __forceinline__ uint32_t key_prefix(uint32_t key, int shift) {
+  return shift >= 32 ? 0u : key >> shift;
+}
+
+// One workgroup per (b, kv) for units with more pages than the register-held
+// select takes (256 threads x 64).  The same choice -- the K largest keys,
+// ties to the lower page, ascending pages -- from passes that re-read the
+// unit's score row (an L2-resident 4 bytes per page) instead of holding it:
+//   1. the smallest and largest key give the prefix every key shares;
+//   2. radix passes of up to 11-bit digits below the resolved prefix: an LDS
+//      histogram of the keys that still carry the prefix and a
+//      digit-descending block scan for the boundary digit, which extends the
+//      prefix; `need` counts the places left for keys that carry it;
+//   3. keys above the final prefix are chosen, and of the keys equal to it the
+//      `need` lowest pages (all of them when need covers them);
+//   4. thread t owns a contiguous run of pages; a block scan of the chosen
+//      counts of the runs gives each run its first output position.
+__global__ void __launch_bounds__(kStreamTopkThreads)
+    topk_stream_kernel(const float* __restrict__ scores, const int32_t* __restrict__ seqlens,
+                       int hkv, int row_pages, ScoreLaunch a) {
+  __shared__ uint32_t hist[1 << kRadixBits];
+  __shared__ uint32_t red_min[kStreamTopkWaves], red_max[kStreamTopkWaves];
+  __shared__ uint32_t scratch[kStreamTopkWaves];
+  __shared__ uint32_t info[3];
+  const int tid = threadIdx.x;
+  const int lane = lane_in_wave();
+  const int wave = tid / kWave;
+  const int kv = blockIdx.x;
+  const int b = blockIdx.y;
+  const int64_t unit = (int64_t)b * hkv + kv;
+  const float* sc = scores + unit * row_pages;
+  int L = seqlens[b];
+  L = L < 0 ? 0 : L;
+  const int64_t pages_l = ((int64_t)L + (1 << a.page_shift) - 1) >> a.page_shift;
+  const int n_pages = pages_l < row_pages ? (int)pages_l : row_pages;
+  const int K = a.num_sel;
+  int32_t* dst = a.page_idx + unit * K;
+  if (n_pages <= K) {
+    for (int i = tid; i < K; i += kStreamTopkThreads) dst[i] = i < n_pages ? i : -1;
+    return;
+  }
+
+  // 1. key range
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int i0 = 0; i0 < n_pages; i0 += kStreamTopkThreads * kStreamUnroll) {
+    float x[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int i = i0 + u * kStreamTopkThreads + tid;
+      x[u] = sc[i < n_pages ? i : n_pages - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const uint32_t k = order_key(x[u]);
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    }
+  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  if (lane == 0) {
+    red_min[wave] = kmin;
+    red_max[wave] = kmax;
+  }
+  for (int i = tid; i < (1 << kRadixBits); i += kStreamTopkThreads) hist[i] = 0u;
+  __syncthreads();
+  kmin = red_min[0];
+  kmax = red_max[0];
+#pragma unroll
+  for (int w = 1; w < kStreamTopkWaves; ++w) {
+    kmin = min(kmin, red_min[w]);
+    kmax = max(kmax, red_max[w]);
+  }
+  const uint32_t diff = kmin ^ kmax;
+  int shift = diff ? 32 - __builtin_clz(diff) : 0;  // bits below the shared prefix
+  uint32_t pre = key_prefix(kmax, shift);
+  uint32_t need = (uint32_t)K;
+  uint32_t ncand = (uint32_t)n_pages;
+
+  // 2. radix passes over the keys that carry the prefix
+  while (need > 0 && need < ncand && shift > 0) {
+    const int nb = shift < kRadixBits ? shift : kRadixBits;
+    const int lo = shift - nb;
+    const uint32_t dmask = (1u << nb) - 1u;
+    for (int i0 = 0; i0 < n_pages; i0 += kStreamTopkThreads * kStreamUnroll) {
+      float x[kStreamUnroll];
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        const int i = i0 + u * kStreamTopkThreads + tid;
+        x[u] = sc[i < n_pages ? i : n_pages - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        const uint32_t k = order_key(x[u]);
+        const bool in = i0 + u * kStreamTopkThreads + tid < n_pages && key_prefix(k, shift) == pre;
+        if (in) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+      }
+    }
+    __syncthreads();
+    // thread t reads `per` digits from the top digit down
+    constexpr int kPerMax = ((1 << kRadixBits) + kStreamTopkThreads - 1) / kStreamTopkThreads;
+    const int nbins = 1 << nb;
+    const int per = (nbins + kStreamTopkThreads - 1) / kStreamTopkThreads;
+    uint32_t cnt[kPerMax];
+    uint32_t run = 0;
+#pragma unroll
+    for (int q = 0; q < kPerMax; ++q) {
+      const int dgt = nbins - 1 - (tid * per + q);
+      cnt[q] = (q < per && dgt >= 0) ? hist[dgt] : 0u;
+      run += cnt[q];
+    }
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan<kStreamTopkWaves>(run, scratch, &total);
+    if (before < need && need <= before + run) {
+      uint32_t acc = before;
+      bool found = false;
+#pragma unroll
+      for (int q = 0; q < kPerMax; ++q) {
+        if (!found && acc + cnt[q] >= need) {
+          info[0] = (uint32_t)(nbins - 1 - (tid * per + q));  // boundary digit
+          info[1] = acc;                                      // keys above it
+          info[2] = cnt[q];                                   // keys on it
+          found = true;
+        }
+        acc += cnt[q];
+      }
+    }
+    __syncthreads();
+    need -= info[1];
+    ncand = info[2];
+    pre = (pre << nb) | info[0];
+    shift = lo;
+    for (int i = tid; i < nbins; i += kStreamTopkThreads) hist[i] = 0u;
+    __syncthreads();  // hist and info are reused by the next pass
+  }
+
+  // 3-4. chosen pages in page order, thread t owning pages [r0, r1)
+  const int per_t = (n_pages + kStreamTopkThreads - 1) / kStreamTopkThreads;
+  const int r0 = min(tid * per_t, n_pages);
+  const int r1 = min(r0 + per_t, n_pages);
+  uint32_t n_above = 0, n_tie = 0;
+  for (int i0 = r0; i0 < r1; i0 += kStreamUnroll) {
+    float x[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) x[u] = sc[min(i0 + u, r1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const uint32_t kp = key_prefix(order_key(x[u]), shift);
+      const bool in = i0 + u < r1;
+      n_above += (in && kp > pre) ? 1u : 0u;
+      n_tie += (in && kp == pre) ? 1u : 0u;
+    }
+  }
+  uint32_t tot_above, tot_tie;
+  uint32_t above_before = block_exclusive_scan<kStreamTopkWaves>(n_above, scratch, &tot_above);
+  uint32_t tie_before = block_exclusive_scan<kStreamTopkWaves>(n_tie, scratch, &tot_tie);
+  for (int i0 = r0; i0 < r1; i0 += kStreamUnroll) {
+    float x[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) x[u] = sc[min(i0 + u, r1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int i = i0 + u;
+      const uint32_t kp = key_prefix(order_key(x[u]), shift);
+      if (i < r1 && kp > pre) {
+        // chosen pages below i: the keys above the prefix, and the tied
+        // pages that fit
+        dst[above_before + min(tie_before, need)] = i;
+        ++above_before;
+      } else if (i < r1 && kp == pre) {
+        if (tie_before < need) dst[above_before + tie_before] = i;
+        ++tie_before;
+      }
+    }
+  }
+}
+
 template <int D, int G, int DEPTH>
 int launch_score(const ScoreLaunch& in, hipStream_t s) {
   // passes per workgroup: enough workgroups to fill the chip (about 1,024),
@@ -356,6 +544,19 @@ int launch_meta_append(const MetaLaunch& a, void* stream) {
   return (int)hipGetLastError();
 }
 
+int launch_topk_only(const ScoreLaunch& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int P = a.meta_max_pages;
+  if (P <= kTopkThreads * 8) return launch_topk<8>(a, s);
+  if (P <= kTopkThreads * 16) return launch_topk<16>(a, s);
+  if (P <= kTopkThreads * 32) return launch_topk<32>(a, s);
+  if (P <= kTopkThreads * 64) return launch_topk<64>(a, s);
+  dim3 grid(a.num_kv_heads, a.batch);
+  hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(kStreamTopkThreads), 0, s, a.scores,
+                     a.seqlens, a.num_kv_heads, a.meta_max_pages, a);
+  return (int)hipGetLastError();
+}
+
 int launch_score_topk(const ScoreLaunch& in, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const ScoreLaunch& a = in;
@@ -363,12 +564,7 @@ int launch_score_topk(const ScoreLaunch& in, void* stream) {
           : a.head_dim == 128 ? launch_score_d<128>(a, s)
                               : (int)hipErrorInvalidValue;
   if (err != 0 || a.page_idx == nullptr) return err;  // scores only
-  const int P = a.meta_max_pages;
-  if (P <= kTopkThreads * 8) return launch_topk<8>(a, s);
-  if (P <= kTopkThreads * 16) return launch_topk<16>(a, s);
-  if (P <= kTopkThreads * 32) return launch_topk<32>(a, s);
-  if (P <= kTopkThreads * 64) return launch_topk<64>(a, s);
-  return (int)hipErrorInvalidValue;
+  return launch_topk_only(a, stream);
 }
 
 int topk_max_pages() { return kTopkThreads * 64; }

@@ -25,9 +25,9 @@
  *     All work is enqueued on `stream` (a hipStream_t; NULL = null stream) and
  *     is complete after the caller synchronises that stream.
  *   - Workspace: size it with da_workspace_size / da_quest_workspace_size.
- *     It holds per-split partial results only (no state survives a call),
- *     needs no initialisation, and must not be shared between calls that may
- *     run concurrently.
+ *     It holds per-split partial results (and, for one call, a page choice)
+ *     only: no state survives a call, it needs no initialisation, and it must
+ *     not be shared between calls that may run concurrently.
  *   - Return value: DA_OK or a negative DA_ERR_* code.  All argument checks run
  *     before anything is enqueued; only DA_ERR_HIP can follow a partial enqueue.
  *     The library never prints and never aborts.
@@ -95,7 +95,9 @@ const char* da_status_string(int status);
  * cache with num_q_heads query heads and the given num_splits (0 = automatic).
  * Writes the size to *bytes_out (host).  The split heuristic depends only on
  * these arguments, so a workspace sized once can be reused for every call with
- * the same shapes.
+ * the same shapes.  With a budget it also covers the choice [B, Hkv, K] int32
+ * that quest_select_sparse_decode_attn keeps there above 16384 pages per unit
+ * when it is given no page_idx.
  */
 int da_workspace_size(const da_kv_cache* kv, int32_t num_q_heads, int32_t budget_tokens,
                       int32_t num_splits, size_t* bytes_out);
@@ -244,7 +246,9 @@ int da_quest_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t meta_ma
  *              scores in the workspace.  Entries p >= P_b are not written.
  *   workspace  (device) >= da_quest_workspace_size(...) bytes when
  *              page_scores is NULL (may be NULL otherwise)
- * Supports meta_max_pages <= 16384.
+ * Up to 16384 pages per (b, kv) the top-K launch holds the unit's scores in
+ * registers; above that a streaming top-K launch (1,024 threads per unit)
+ * re-reads the score row once per radix pass.  Same choice either way.
  */
 int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_pages,
                           const int32_t* seqlens, int32_t batch, int32_t num_q_heads,
@@ -268,7 +272,7 @@ int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_page
  *   kv         (host)   cache description (contiguous or paged); S =
  *              kv->page_size in {8, 16, 32, 64}; D and Hkv from kv
  *   meta       (device) fp16 [B, Hkv, meta_max_pages, 2, D], updated in place;
- *              meta_max_pages * S >= per-sequence capacity, <= 16384
+ *              meta_max_pages * S >= per-sequence capacity
  *   seqlens    (device) int32 [B], lengths after this step (L_b >= 1 appends;
  *              L_b = 0 appends nothing)
  *   k_new, v_new (device) fp16 [B, Hkv, D], both required
@@ -314,15 +318,19 @@ int quest_sparse_decode_attn(const void* q, const da_kv_cache* kv, const int32_t
  *              quest_page_score_topk or quest_append_score_topk (with page_idx
  *              NULL, for the scores alone); entries p >= P_b are ignored.
  *   meta_max_pages  row width of page_scores; meta_max_pages * S >= the
- *              per-sequence capacity; <= 16384
+ *              per-sequence capacity.  Above 16384 pages per (b, kv) the call
+ *              runs the streaming top-K launch of quest_page_score_topk
+ *              first and the attention over its choice second (written to
+ *              page_idx, or to the workspace without it): the same choice
+ *              and output, one launch more.
  *   page_idx   (device) int32 [B, Hkv, K] out: the choice, as
  *              quest_page_score_topk writes it; or NULL
  *   budget_tokens, q, kv, seqlens, num_q_heads, scale, out, workspace
  *              (da_workspace_size(kv, Hq, budget_tokens, num_splits) bytes),
  *              num_splits, stream: as quest_sparse_decode_attn.
  * Returns DA_ERR_NULL if page_scores is NULL (B > 0), DA_ERR_SHAPE if
- * meta_max_pages does not cover the capacity, DA_ERR_UNSUPPORTED above 16384
- * pages, otherwise as quest_sparse_decode_attn.
+ * meta_max_pages does not cover the capacity (or, above 16384 pages, B or Hkv
+ * exceeds 65535), otherwise as quest_sparse_decode_attn.
  */
 int quest_select_sparse_decode_attn(const void* q, const da_kv_cache* kv,
                                     const int32_t* seqlens, const float* page_scores,

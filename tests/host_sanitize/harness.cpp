@@ -240,8 +240,9 @@ void score_checks() {
                 DA_ERR_BUDGET);
   EXPECT_STATUS(call(2, 32, 8, 96, 16, 256, 256, fake_i(13), nullptr, fake(6), need),
                 DA_ERR_UNSUPPORTED);
-  EXPECT_STATUS(call(2, 32, 8, 128, 16, 256, 16385, fake_i(13), nullptr, fake(6), kBigWs),
-                DA_ERR_UNSUPPORTED);
+  // above 16384 pages per unit the same call runs the streaming top-K
+  EXPECT_STATUS(call(2, 32, 8, 128, 16, 256, 16385, fake_i(13), nullptr, fake(6), kBigWs), DA_OK);
+  CHECK(da::g_stub.last == da::StubRecord::kScore && da::g_stub.score.meta_max_pages == 16385);
   EXPECT_STATUS(call(2, 32, 8, 128, 16, 256, 256, nullptr, nullptr, fake(6), need),
                 DA_ERR_NULL);   // nothing to output
   EXPECT_STATUS(call(2, 32, 8, 128, 16, 256, 256, nullptr, static_cast<float*>(fake(14)),
@@ -281,9 +282,35 @@ void sparse_checks() {
   CHECK(da::g_stub.attn.sel_scores != nullptr && da::g_stub.attn.sel_row == 256);
   EXPECT_STATUS(select(kv, nullptr, 256, 256), DA_ERR_NULL);
   EXPECT_STATUS(select(kv, static_cast<float*>(fake(14)), 255, 256), DA_ERR_SHAPE);
+  // more pages per unit than the attention launch selects itself: the
+  // streaming top-K writes the choice to the workspace (no page_idx), then
+  // the attention reads it as a given list
+  const long before = da::g_stub.launches;
   EXPECT_STATUS(select(contiguous(2, 8, 128, 1 << 20), static_cast<float*>(fake(14)), 1 << 16,
                        256),
-                DA_ERR_UNSUPPORTED);
+                DA_OK);
+  CHECK(da::g_stub.launches == before + 2 && da::g_stub.last == da::StubRecord::kAttn);
+  CHECK(da::g_stub.topk.meta_max_pages == 1 << 16 && da::g_stub.topk.num_sel == 16);
+  CHECK(da::g_stub.topk.scores == static_cast<float*>(fake(14)));
+  CHECK(da::g_stub.attn.sel_scores == nullptr && da::g_stub.attn.page_idx != nullptr);
+  CHECK(da::g_stub.attn.page_idx == da::g_stub.topk.page_idx);
+  {
+    // the choice sits after the partials, inside the workspace the size query asks for
+    da_kv_cache big = contiguous(2, 8, 128, 1 << 20);
+    size_t need = 0;
+    EXPECT_STATUS(da_workspace_size(&big, 32, 256, 0, &need), DA_OK);
+    const char* ws0 = static_cast<const char*>(fake(6));
+    const char* idx = reinterpret_cast<const char*>(da::g_stub.topk.page_idx);
+    CHECK(idx >= ws0 + 2 * 8 * da::g_stub.attn.max_splits * 4 * 2 * sizeof(float));
+    CHECK(idx + 2 * 8 * 16 * sizeof(int32_t) == ws0 + need);
+  }
+  // with page_idx the choice goes there
+  EXPECT_STATUS(quest_select_sparse_decode_attn(fake(4), &kv, fake_i(7),
+                                                static_cast<float*>(fake(14)), 1 << 16, 256, 32,
+                                                0.1f, fake_i(15), fake(5), fake(6), kBigWs, 0,
+                                                nullptr),
+                DA_OK);
+  CHECK(da::g_stub.topk.page_idx == fake_i(15) && da::g_stub.attn.page_idx == fake_i(15));
 }
 
 void check_checks() {

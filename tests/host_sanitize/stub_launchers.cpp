@@ -42,6 +42,12 @@ int launch_score_topk(const ScoreLaunch& p, void*) {
   ++g_stub.launches;
   return 0;
 }
+int launch_topk_only(const ScoreLaunch& p, void*) {
+  g_stub.topk = p;
+  g_stub.last = StubRecord::kTopk;
+  ++g_stub.launches;
+  return 0;
+}
 int launch_repeat_kv(const RepeatLaunch& p, void*) {
   g_stub.repeat = p;
   g_stub.last = StubRecord::kRepeat;

@@ -7,12 +7,13 @@
 namespace da {
 
 struct StubRecord {
-  enum Kind { kNone, kAttn, kMeta, kScore, kRepeat, kCheck, kCalibration };
+  enum Kind { kNone, kAttn, kMeta, kScore, kTopk, kRepeat, kCheck, kCalibration };
   Kind last = kNone;
   long launches = 0;
   AttnLaunch attn{};
   MetaLaunch meta{};
   ScoreLaunch score{};
+  ScoreLaunch topk{};
   RepeatLaunch repeat{};
 };
 

@@ -93,7 +93,8 @@ def test_select_sparse_validation_codes(lib):
     assert call(budget=0) == -4
     assert call(meta_pages=255) == -2                          # 255 * 16 < capacity 4096
     assert call(meta_pages=0) == -2
-    assert call(desc=_desc(capacity=1 << 20), meta_pages=1 << 16) == -3   # > 16384 pages
+    # > 16384 pages per unit: streaming top-K, then attention (no device here)
+    assert call(desc=_desc(capacity=1 << 20), meta_pages=1 << 16) == -6
     assert call(desc=_desc(page_size=12)) == -3
     assert call(hq=30) == -2
     assert call(ws_bytes=16) == -5
@@ -159,7 +160,7 @@ def test_quest_validation_codes(lib):
     assert st == -3                                            # S = 12
     st = lib.quest_page_score_topk(P(FAKE), P(FAKE), 1 << 15, P(FAKE), 1, 32, 8, 128, 16, 256,
                                    P(FAKE), P(FAKE), None, 0, None)
-    assert st == -3                                            # too many pages for top-K
+    assert st == -6                    # 32768 pages: streaming top-K, no device here
     st = lib.quest_page_score_topk(P(FAKE), P(FAKE), 256, P(FAKE), 1, 32, 8, 128, 16, 256,
                                    P(FAKE), None, P(FAKE), 16, None)
     assert st == -5                                            # score workspace too small
@@ -202,7 +203,10 @@ def test_workspace_sizes(lib):
     small = size(_desc(batch=1))
     big = size(_desc(batch=8))
     assert 0 < small <= big
-    assert size(_desc(), budget=2048) <= size(_desc())
+    # the selected-page stream: fewer partials, plus room for the choice
+    d = _desc()
+    choice = d.batch * d.num_kv_heads * (2048 // d.page_size) * 4
+    assert size(_desc(), budget=2048) <= size(_desc()) + choice
     assert size(_desc(), splits=1) < size(_desc(), splits=64)
     out = ctypes.c_size_t()
     assert lib.da_quest_workspace_size(8, 8, 8192, ctypes.byref(out)) == 0
@@ -250,9 +254,14 @@ def _planned_splits(units, max_keys, page_list, num_splits=0):
     return -(-tiles // tps)
 
 
-def _plan_bytes(units, splits, rows, d):
+def _plan_bytes(units, splits, rows, d, k_sel=0):
+    """Partials (m, l) and o; with a page budget also the choice, K int32 per
+    unit, after the 256-byte aligned partials."""
     ml = -(-(units * splits * rows * 2 * 4) // 256) * 256
-    return ml + units * splits * rows * d * 4
+    o = units * splits * rows * d * 4
+    if k_sel == 0:
+        return ml + o
+    return ml + -(-o // 256) * 256 + units * k_sel * 4
 
 
 # (desc fields, Hq, budget tokens, explicit splits, page list, longest key stream, splits)
@@ -278,7 +287,9 @@ def test_workspace_follows_the_split_plan(lib, fields, hq, budget, splits, page_
     assert got_splits == want_splits  # the rule itself, on the workloads' shapes
     out = ctypes.c_size_t()
     assert lib.da_workspace_size(ctypes.byref(desc), hq, budget, splits, ctypes.byref(out)) == 0
-    assert out.value == _plan_bytes(units, want_splits, hq // desc.num_kv_heads, desc.head_dim)
+    k_sel = budget // desc.page_size if budget else 0
+    assert out.value == _plan_bytes(units, want_splits, hq // desc.num_kv_heads, desc.head_dim,
+                                    k_sel)
 
 
 def _noalloc(lib, desc, hq=32, q=FAKE, seqlens=FAKE, out=FAKE, splits=0):

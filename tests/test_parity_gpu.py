@@ -385,10 +385,15 @@ def test_score_topk_parity(da, page_size, budget, g, d, cap, lens):
     (3001, 64, 2999),       # 16 items per thread, ragged
     (16384, 1000, 16384),   # the maximum: 64 items per thread
     (12000, 5, 11111),      # 64 items per thread, ragged, small K
+    (16385, 300, 16385),    # one page past the register-held select: streaming top-K
+    (65536, 256, 65536),    # 1M tokens at S = 16
+    (40000, 2000, 39001),   # ragged, large K
+    (50000, 3, 49999),      # small K
 ])
 def test_topk_large_page_counts(da, n_pages, k_pages, seqlen_pages):
-    """Score + top-K on random metadata up to the supported maximum of
-    16384 pages per (b, kv): every item-per-thread width of the select."""
+    """Score + top-K on random metadata: every item-per-thread width of the
+    register-held select (up to 16384 pages per (b, kv)) and the streaming
+    select above it."""
     s, d, g, hkv = 8, 64, 2, 2
     rng = np.random.default_rng(n_pages)
     a = rng.standard_normal((1, hkv, n_pages, d), dtype=np.float32)
@@ -801,4 +806,16 @@ def test_topk_all_scores_equal(da):
 
 def test_topk_many_boundary_ties(da):
     idx, want = _topk_case(da, "many_ties", k_pages=50)
+    assert np.array_equal(idx, want)
+
+
+@pytest.mark.parametrize("n_pages", [8192, 20000])
+@pytest.mark.parametrize("kind,k_pages", [("equal", 256), ("many_ties", 50), ("many_ties", 256)])
+def test_topk_ties_at_large_page_counts(da, kind, k_pages, n_pages):
+    """The same tie cases at 8192 pages (32 items per thread) and at 20000
+    (the streaming select): every page tied, and 100 tied pages over the
+    rest straddling the K-th place."""
+    idx, want = _topk_case(da, kind, n_pages=n_pages, k_pages=k_pages, seed=710)
+    if kind == "equal":
+        assert list(want[0, 0]) == list(range(k_pages))
     assert np.array_equal(idx, want)

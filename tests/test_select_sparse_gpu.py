@@ -6,8 +6,9 @@ The fused call must make exactly the choice of quest_page_score_topk's top-K
 launch and produce bit-identical output to quest_sparse_decode_attn over that
 choice (same arithmetic, same split plan): both are compared element by
 element, on every items-per-thread width of the in-kernel top-K (up to 16384
-pages), with ragged and empty sequences, K >= P_b, explicit split counts and
-a paged cache.  One case is also compared with the fp64 oracle directly.
+pages) and beyond it (where the call runs the streaming top-K launch first),
+with ragged and empty sequences, K >= P_b, explicit split counts and a paged
+cache.  Two cases are also compared with the fp64 oracle directly.
 """
 
 import numpy as np
@@ -60,6 +61,7 @@ SELECT_CASES = [
     (16, 512, 4, 64, [16384 * 4 - 5, 70], 16384 * 4, 0),    # 4096 pages: 16 per thread
     (16, 1024, 2, 64, [8192 * 16, 8192 * 16 - 100], 8192 * 16, 0),  # 8192: 32 per thread
     (8, 4096, 1, 64, [16384 * 8 - 1], 16384 * 8, 1),        # 16384: 64 per thread, 1 split
+    (8, 2048, 1, 64, [20000 * 8 - 3, 5000], 20000 * 8, 0),  # 20000: streaming top-K first
 ]
 
 
@@ -125,6 +127,40 @@ def test_select_sparse_parity_with_oracle(da):
     want = oquest.sparse_decode_attention(case.q, case.k, case.v, case.seqlens, host(idx),
                                           page_size, case.scale)
     assert max_err(host(out), want) <= ATOL
+
+
+def test_select_beyond_register_held_top_k(da):
+    """More than 16384 pages per unit: the call runs the streaming top-K, then
+    the attention over its choice, written to page_idx or (without it) to the
+    workspace.  Both give the same output, the choice agrees with the oracle's
+    under the near-tie rule, and the output with the oracle's attention over
+    the GPU's choice."""
+    page_size, budget, g = 16, 1024, 4
+    cap = 16384 * 16 + 1600                 # 16484 pages
+    lens = [cap, cap - 700]
+    case = workloads.dense_case(940, 2, g, 1, 64, cap, lens, plant_pages=6,
+                                plant_page_size=page_size)
+    n_meta = cap // page_size
+    meta = run_meta_bulk(da, case, page_size, n_meta)
+    q, k, v, ln = dev(case.q), dev(case.k), dev(case.v), dev(case.seqlens)
+    scores = torch.empty((2, 1, n_meta), dtype=torch.float32, device=DEV)
+    da.quest_page_score_topk(q, meta, ln, page_size=page_size, budget_tokens=budget,
+                             page_scores=scores, select=False)
+    idx = torch.full((2, 1, budget // page_size), -7, dtype=torch.int32, device=DEV)
+    a = da.quest_select_sparse_decode_attn(q, k, v, ln, scores, budget_tokens=budget,
+                                           page_size=page_size, page_idx=idx)
+    b = da.quest_select_sparse_decode_attn(q, k, v, ln, scores, budget_tokens=budget,
+                                           page_size=page_size)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    want_meta = oquest.build_metadata(case.k, case.seqlens, page_size, n_meta)
+    want_scores = oquest.page_scores(case.q, want_meta, case.seqlens, page_size)
+    want_idx = oquest.select_pages(want_scores, case.seqlens, page_size, budget // page_size)
+    check_selection(host(idx), host(scores).astype(np.float64), want_idx, want_scores,
+                    case.seqlens, page_size, budget // page_size)
+    want = oquest.sparse_decode_attention(case.q, case.k, case.v, case.seqlens, host(idx),
+                                          page_size, case.scale)
+    assert max_err(host(a), want) <= ATOL
 
 
 def test_scores_only_mode(da):
