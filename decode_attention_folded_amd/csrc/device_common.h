@@ -152,8 +152,10 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 }
 
 // Exclusive prefix sum over a block of NWAVES waves; *total gets the block
-// sum.  Must be reached by every thread of the block.
-template <int NWAVES>
+// sum.  Must be reached by every thread of the block.  Without the trailing
+// barrier (TRAILING = false) the caller must pass another barrier before
+// `scratch` is written again.
+template <int NWAVES, bool TRAILING = true>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch,
                                                          uint32_t* total) {
   const int lane = lane_in_wave();
@@ -168,7 +170,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     if (w < wave) base += s;
     sum += s;
   }
-  __syncthreads();
+  if constexpr (TRAILING) __syncthreads();
   *total = sum;
   return base + inc - v;
 }

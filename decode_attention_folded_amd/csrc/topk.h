@@ -30,8 +30,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // Top-K of one (b, kv) unit's page scores by one workgroup of 256 threads.
 // Thread t holds items i = k * 256 + t (k < R), raw[k] = score of item i
 // (anything past the valid pages, which are masked); the selected set is kept
-// as an LDS bitmap whose words are written with wave ballots (item i in word
-// i / 32).
+// as an LDS bitmap (item i in word i / 32).
 //   1. keys = order-preserving u32 of the scores; skip the bits shared by the
 //      smallest and largest key;
 //   2. radix passes on 11-bit digits: LDS histogram of the remaining
@@ -83,8 +82,10 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
     red_min[wave] = kmin;
     red_max[wave] = kmax;
   }
-  // the first pass's histogram is cleared under the same barrier
+  // the first pass's histogram and the bitmap are cleared under the same
+  // barrier
   for (int i = tid; i < (1 << kRadixBits); i += kTopkThreads) hist[i] = 0u;
+  for (int w = tid; w < NW; w += kTopkThreads) selbits[w] = 0u;
   __syncthreads();
   kmin = red_min[0];
   kmax = red_max[0];
@@ -98,16 +99,24 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
   uint32_t need = (uint32_t)K;
   uint32_t ncand = (uint32_t)n_pages;
 
+  bool first = true;
   while (need > 0 && need < ncand && shift > 0 && ncand > (uint32_t)kMaxRankCand) {
     const int nb = shift < kRadixBits ? shift : kRadixBits;
     shift -= nb;
     const uint32_t nbins = 1u << nb;
+    if (first) {  // every valid item is a candidate: no per-slot test
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const bool c = (cand >> k) & 1;
-      if (__ballot(c) != 0)  // wave-uniform: skip slots with no candidate
-        atomicAdd(&hist[(key[k] >> shift) & (nbins - 1)], c ? 1u : 0u);
+      for (int k = 0; k < R; ++k)
+        atomicAdd(&hist[(key[k] >> shift) & (nbins - 1)], ((cand >> k) & 1) ? 1u : 0u);
+    } else {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const bool c = (cand >> k) & 1;
+        if (__ballot(c) != 0)  // wave-uniform: skip slots with no candidate
+          atomicAdd(&hist[(key[k] >> shift) & (nbins - 1)], c ? 1u : 0u);
+      }
     }
+    first = false;
     __syncthreads();
     // thread t sums a run of `per` digits taken from the top digit down,
     // keeping the counts in registers for the boundary search
@@ -122,7 +131,8 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
       run += cnt[q];
     }
     uint32_t total;
-    const uint32_t before = block_exclusive_scan<kTopkWaves>(run, scratch, &total);
+    // (the barrier after the boundary search also guards `scratch`)
+    const uint32_t before = block_exclusive_scan<kTopkWaves, false>(run, scratch, &total);
     if (before < need && need <= before + run) {
       uint32_t acc = before;
       bool found = false;
@@ -150,23 +160,22 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
     }
     need -= above;
     ncand = on;
-    // the next pass's histogram (nobody reads this one any more)
-    for (int i = tid; i < (int)nbins; i += kTopkThreads) hist[i] = 0u;
-    __syncthreads();  // hist and info are reused by the next pass
+    if (need > 0 && need < ncand && shift > 0 && ncand > (uint32_t)kMaxRankCand) {
+      // another pass: its histogram (nobody reads this one any more)
+      for (int i = tid; i < (int)nbins; i += kTopkThreads) hist[i] = 0u;
+      __syncthreads();  // hist and info are reused by the next pass
+    }
   }
   if (need >= ncand) {  // the remaining candidates all fit
     take |= cand;
     cand = 0;
   }
 
-  // chosen items -> bitmap (each (slot, wave) owns two words)
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    const uint64_t m = __ballot((take >> k) & 1);
-    if (lane == 0) {
-      selbits[k * 8 + 2 * wave] = (uint32_t)m;
-      selbits[k * 8 + 2 * wave + 1] = (uint32_t)(m >> 32);
-    }
+  // chosen items -> bitmap: each thread sets the bits of its own chosen
+  // items (K of all items, so about K / 256 per thread)
+  for (Mask t = take; t != 0; t &= t - 1) {
+    const int i = __builtin_ctzll((uint64_t)t) * kTopkThreads + tid;
+    atomicOr(&selbits[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
 
@@ -177,8 +186,8 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
       // count (plain stores; an LDS atomic per slot costs a round trip each),
       // then rank each one
       uint32_t listed_total;
-      uint32_t pos = block_exclusive_scan<kTopkWaves>((uint32_t)__builtin_popcountll(cand),
-                                                      scratch, &listed_total);
+      uint32_t pos = block_exclusive_scan<kTopkWaves, false>(
+          (uint32_t)__builtin_popcountll(cand), scratch, &listed_total);
 #pragma unroll
       for (int k = 0; k < R; ++k) {
         if ((cand >> k) & 1) {  // ncand <= 64 candidates exist: pos < 64
@@ -225,7 +234,7 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
         if (w < NW) mine += __builtin_popcount(candbits[w]);
       }
       uint32_t total;
-      uint32_t rank = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
+      uint32_t rank = block_exclusive_scan<kTopkWaves, false>(mine, scratch, &total);
 #pragma unroll
       for (int q = 0; q < WPT; ++q) {
         const int w = tid * WPT + q;
@@ -252,7 +261,8 @@ __device__ __forceinline__ void select_top_k(const float (&raw)[R], int n_pages,
     if (w < NW) mine += __builtin_popcount(selbits[w]);
   }
   uint32_t total;
-  uint32_t pos = block_exclusive_scan<kTopkWaves>(mine, scratch, &total);
+  // (the selection's last use of `scratch`)
+  uint32_t pos = block_exclusive_scan<kTopkWaves, false>(mine, scratch, &total);
 #pragma unroll
   for (int q = 0; q < WPT; ++q) {
     const int w = tid * WPT + q;
