@@ -16,6 +16,9 @@
 namespace {
 
 constexpr int kMaxGridDim = 65535;
+// Pages per (b, kv) row of the Quest metadata and scores: keeps the kernels'
+// 32-bit page arithmetic (index plus a few thousand) clear of overflow.
+constexpr int kMaxMetaPages = 1 << 28;
 // Split plan: enough key tiles per workgroup that the grid is about one
 // workgroup per CU (256 CUs), longer chunks where the stream allows.  Measured
 // against 384, 512, 768 and 1024: equal on the dense and paged workloads
@@ -367,7 +370,8 @@ int quest_meta_append(const da_kv_cache* kv, void* meta, int32_t meta_max_pages,
   if ((k_new == nullptr) != (v_new == nullptr)) return DA_ERR_NULL;
   if (k_new != nullptr && n_new != 1) return DA_ERR_SHAPE;
   if (n_new < 1) return DA_ERR_SHAPE;
-  if (meta_max_pages < 1 || (int64_t)meta_max_pages * s.page_size < s.capacity)
+  if (meta_max_pages < 1 || meta_max_pages > kMaxMetaPages ||
+      (int64_t)meta_max_pages * s.page_size < s.capacity)
     return DA_ERR_SHAPE;
   if (s.batch == 0) return DA_OK;  // nothing to read or write
   if (meta == nullptr || seqlens == nullptr || kv->k == nullptr) return DA_ERR_NULL;
@@ -403,7 +407,8 @@ int quest_meta_append(const da_kv_cache* kv, void* meta, int32_t meta_max_pages,
 int da_quest_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t meta_max_pages,
                             size_t* bytes_out) {
   if (bytes_out == nullptr) return DA_ERR_NULL;
-  if (batch < 0 || num_kv_heads < 1 || meta_max_pages < 1) return DA_ERR_SHAPE;
+  if (batch < 0 || num_kv_heads < 1 || meta_max_pages < 1 || meta_max_pages > kMaxMetaPages)
+    return DA_ERR_SHAPE;
   *bytes_out = align256((size_t)batch * num_kv_heads * meta_max_pages * sizeof(float));
   if (*bytes_out == 0) *bytes_out = 256;
   return DA_OK;
@@ -414,7 +419,8 @@ int quest_page_score_topk(const void* q, const void* meta, int32_t meta_max_page
                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                           int32_t budget_tokens, int32_t* page_idx, float* page_scores,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  if (batch < 0 || num_kv_heads < 1 || num_q_heads < 1 || meta_max_pages < 1)
+  if (batch < 0 || num_kv_heads < 1 || num_q_heads < 1 || meta_max_pages < 1 ||
+      meta_max_pages > kMaxMetaPages)
     return DA_ERR_SHAPE;
   if (batch > kMaxGridDim || num_kv_heads > kMaxGridDim) return DA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return DA_ERR_SHAPE;
@@ -471,7 +477,8 @@ int quest_append_score_topk(const void* q, const da_kv_cache* kv, void* meta,
   if (st != DA_OK) return st;
   if (!is_pow2_in(s.page_size, 8, 64)) return DA_ERR_UNSUPPORTED;
   if (budget_tokens <= 0 || budget_tokens % s.page_size != 0) return DA_ERR_BUDGET;
-  if (meta_max_pages < 1 || (int64_t)meta_max_pages * s.page_size < s.capacity)
+  if (meta_max_pages < 1 || meta_max_pages > kMaxMetaPages ||
+      (int64_t)meta_max_pages * s.page_size < s.capacity)
     return DA_ERR_SHAPE;
   if (s.batch == 0) return DA_OK;  // nothing to read or write
   if (q == nullptr || meta == nullptr || seqlens == nullptr || k_new == nullptr ||
@@ -526,7 +533,8 @@ int quest_select_sparse_decode_attn(const void* q, const da_kv_cache* kv,
   if (st != DA_OK) return st;
   st = check_budget(s, budget_tokens);
   if (st != DA_OK) return st;
-  if (meta_max_pages < 1 || (int64_t)meta_max_pages * s.page_size < s.capacity)
+  if (meta_max_pages < 1 || meta_max_pages > kMaxMetaPages ||
+      (int64_t)meta_max_pages * s.page_size < s.capacity)
     return DA_ERR_SHAPE;  // every page that can hold a valid token has a score
   if (s.batch > 0 && page_scores == nullptr) return DA_ERR_NULL;
   PageSelect sel;

@@ -202,7 +202,8 @@ int gqa_repeat_kv(const da_kv_cache* kv, int32_t num_q_heads, const int32_t* seq
  *
  *   kv         (host)   cache description; S = kv->page_size in {8,16,32,64}
  *   meta       (device) fp16 [B, Hkv, meta_max_pages, 2, D]; [...,0,:] = min,
- *              [...,1,:] = max.  meta_max_pages * S >= per-sequence capacity.
+ *              [...,1,:] = max.  meta_max_pages * S >= per-sequence capacity;
+ *              meta_max_pages <= 2^28 in every quest_* call (DA_ERR_SHAPE).
  *   seqlens    (device) int32 [B] (lengths after this update)
  *   n_new      keys [L_b - n_new, L_b) are folded in, in order.  A key at a
  *              page start (t mod S == 0) resets that page to (k, k); any other

@@ -240,6 +240,8 @@ void score_checks() {
                 DA_ERR_BUDGET);
   EXPECT_STATUS(call(2, 32, 8, 96, 16, 256, 256, fake_i(13), nullptr, fake(6), need),
                 DA_ERR_UNSUPPORTED);
+  EXPECT_STATUS(call(2, 32, 8, 128, 16, 256, (1 << 28) + 1, fake_i(13), nullptr, fake(6), kBigWs),
+                DA_ERR_SHAPE);  // more pages than the kernels' index arithmetic allows
   // above 16384 pages per unit the same call runs the streaming top-K
   EXPECT_STATUS(call(2, 32, 8, 128, 16, 256, 16385, fake_i(13), nullptr, fake(6), kBigWs), DA_OK);
   CHECK(da::g_stub.last == da::StubRecord::kScore && da::g_stub.score.meta_max_pages == 16385);
