@@ -217,3 +217,24 @@ def test_full_quest_gqa_128k_step(da):
         assert max_err(got[bi:bi + 1, rows], want) <= ATOL, (bi, kv)
         want_dense = oracle.decode_attention(q_u, k_u, v_u, [L], 1 / math.sqrt(d))
         assert max_err(got_dense[bi:bi + 1, rows], want_dense) <= ATOL, (bi, kv)
+
+
+def test_million_key_sequence_many_merge_rounds(da):
+    """The long-context extreme: one sequence of 2^20 keys (plus the step's
+    append) under the automatic split plan, which gives it 256 splits -- more
+    than one round of the merge's 48-split loads.  Every output element
+    against the fp64 oracle over all 2^20 keys."""
+    b, hq, hkv, d, cap = 1, 4, 1, 64, 1 << 20
+    case = workloads.dense_case(1234, b, hq, hkv, d, cap, [cap], with_new=True, poison=False)
+    q, k, v = (torch.from_numpy(x).to(DEV) for x in (case.q, case.k, case.v))
+    kn, vn = torch.from_numpy(case.k_new).to(DEV), torch.from_numpy(case.v_new).to(DEV)
+    lens = torch.from_numpy(case.seqlens).to(DEV)
+    ws = da.Workspace()
+    out = da.gqa_decode_attn(q, k, v, lens, k_new=kn, v_new=vn, workspace=ws)
+    torch.cuda.synchronize()
+    k2, v2 = oracle.append_kv(case.k, case.v, case.seqlens, case.k_new, case.v_new)
+    want = oracle.decode_attention(case.q, k2, v2, case.seqlens, case.scale)
+    assert max_err(host(out), want) <= ATOL
+    # the plan really spans several merge rounds: partials of more than 48
+    # splits per (b, kv) unit
+    assert da.workspace_bytes(k, v, b, hq) >= b * hkv * 49 * hq * (d + 2) * 4
