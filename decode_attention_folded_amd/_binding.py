@@ -567,10 +567,15 @@ def check_cache(k_cache, v_cache, seqlens, *, page_table=None, page_size=0, repo
     _need(seqlens, "seqlens", torch.int32, 1)
     desc = _kv_desc(k_cache, v_cache, seqlens.shape[0], page_table, page_size)
     if report is None:
-        report = torch.zeros(4, dtype=torch.int32, device=seqlens.device)
+        # no fill: the kernel writes all four entries (a fill on another
+        # stream than the check's could land after it)
+        report = torch.empty(4, dtype=torch.int32, device=seqlens.device)
     _need(report, "report", torch.int32, 1)
     if report.numel() < 4:
         raise ValueError("report must hold 4 int32")
+    if seqlens.numel() == 0:  # nothing to check; the library writes nothing
+        report.copy_(torch.tensor([0, 0, -1, 0], dtype=torch.int32))
+        return report
     _check(lib.da_check_cache(ctypes.byref(desc), _ptr(seqlens), _ptr(report),
                               _stream_handle(seqlens.device, stream)), "da_check_cache")
     return report
