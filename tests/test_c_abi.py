@@ -21,6 +21,14 @@ def _run():
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
 def test_c_program_links_and_reports_no_device():
+    if not os.path.exists(EXE):  # a CPU checkout that skipped build(): build it here
+        import sys
+        sys.path.insert(0, ROOT)
+        from decode_attention_folded_amd import _binding, build
+        if not os.path.exists(_binding.library_path()):
+            build.build(verbose=False)
+        import __graft_entry__
+        __graft_entry__.build_c_abi_check(verbose=False)
     r = _run()
     assert r.returncode == 2, (r.stdout, r.stderr)
     assert "no HIP device" in r.stderr
