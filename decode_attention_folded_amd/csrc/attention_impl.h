@@ -135,17 +135,19 @@ struct Stage {
 // order (log-sum-exp).  One thread per output element; D is a multiple of 64,
 // so every wave works on one row.  Lane s of a wave loads split s's (m, l) of
 // that row and the values reach the other lanes through readlane, so a round
-// of kBatch splits is 1 + kBatch loads per lane: within the 63 loads a wave
-// can keep in flight, so the round costs one memory round trip.  The first
+// of KB splits is 1 + KB loads per lane: within the 63 loads a wave can keep
+// in flight, so the round costs one memory round trip.  The launch picks KB
+// (8, 16 or 48) to cover the plan's splits with as few loads as possible.  The first
 // round is read before `get_nsplit` is called (it may wait for the valid
 // length).  Splits past the valid ones get zero weight, so stale workspace
 // contents never enter the sums.
-template <int D, int G, int NT, typename NSplitFn>
+template <int D, int G, int NT, int KB, typename NSplitFn>
 __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float* part_ml,
                                                const float* part_o, int max_splits, int64_t unit,
                                                NSplitFn get_nsplit) {
   static_assert(NT == G * D && D % kWave == 0, "one thread per output element, one row per wave");
-  constexpr int kBatch = 48;  // splits per round of loads
+  constexpr int kBatch = KB;  // splits per round of loads (at most 48)
+  static_assert(KB >= 1 && KB <= 48, "splits per round");
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + unit * max_splits * G;
   const float* po = part_o + unit * max_splits * G * D;
   f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;
@@ -765,14 +767,14 @@ __global__ void __launch_bounds__(kThreads)
 // with one round of loads (merge_partials).
 // Leading scalar arguments as in the attention kernel: what the first round
 // of partial loads needs.
-template <int D, int G, bool SPARSE>
+template <int D, int G, bool SPARSE, int KB>
 __global__ void __launch_bounds__(G * D)
     merge_kernel(const float* __restrict__ part_ml, const float* __restrict__ part_o,
                  const int32_t* __restrict__ seqlens, int max_splits, int hkv, AttnLaunch a) {
   const int kv = blockIdx.x;
   const int b = blockIdx.y;
   const int64_t unit = (int64_t)b * hkv + kv;
-  merge_partials<D, G, G * D>(a, part_ml, part_o, max_splits, unit,
+  merge_partials<D, G, G * D, KB>(a, part_ml, part_o, max_splits, unit,
                               [&] { return stream_info(a, seqlens, b, SPARSE).nsplit; });
 }
 
@@ -803,8 +805,18 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
   }
   const int err = (int)hipGetLastError();
   if (err != 0 || a.max_splits <= 1) return err;
-  hipLaunchKernelGGL((merge_kernel<D, G, SPARSE>), dim3(a.num_kv_heads, a.batch), dim3(G * D), 0,
-                     stream, a.part_ml, a.part_o, a.seqlens, a.max_splits, a.num_kv_heads, a);
+  // a round of loads covers at most max_splits splits: no loads past them
+  auto merge = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(a.num_kv_heads, a.batch), dim3(G * D), 0, stream, a.part_ml,
+                       a.part_o, a.seqlens, a.max_splits, a.num_kv_heads, a);
+  };
+  if (a.max_splits <= 8) {
+    merge(merge_kernel<D, G, SPARSE, 8>);
+  } else if (a.max_splits <= 16) {
+    merge(merge_kernel<D, G, SPARSE, 16>);
+  } else {
+    merge(merge_kernel<D, G, SPARSE, 48>);
+  }
   return (int)hipGetLastError();
 }
 
