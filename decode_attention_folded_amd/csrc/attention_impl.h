@@ -77,12 +77,14 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kTileKeys = 16;
 // Key tiles per workgroup chunk, at most: 128 when the chunk reads a page
-// list (paged cache or chosen pages; the list is staged in LDS), 256 for a
+// list (paged cache or chosen pages; the list is staged in LDS), 512 for a
 // contiguous cache.  Measured on MI355X: contiguous 128K dense attention
-// 672 us at 128, 642 at 256, 635 at 512; the variable-length paged batch 706,
-// 715 and 761 us (coarser chunks leave a longer tail of unequal sequences).
+// 672 us at 128, 642 at 256, 634 at 512, 636 at 1024 (fewer workgroup
+// start-ups and partials); the variable-length paged batch 706, 715 and
+// 761 us at 128, 256 and 512 (coarser chunks leave a longer tail of unequal
+// sequences).
 constexpr int kMaxTilesPerSplit = 128;
-constexpr int kMaxTilesPerSplitContiguous = 256;
+constexpr int kMaxTilesPerSplitContiguous = 512;
 constexpr int kMinPageSize = 8;
 // pages (or chosen-page entries) one chunk can touch
 constexpr int kMaxChunkPages = kMaxTilesPerSplit * kTileKeys / kMinPageSize + 2;

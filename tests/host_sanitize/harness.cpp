@@ -382,7 +382,7 @@ void fuzz(uint64_t seed, int rounds) {
       if (kv.batch > 0) {
         const da::AttnLaunch& a = da::g_stub.attn;
         CHECK((int64_t)a.max_splits * a.batch * a.num_kv_heads <= INT32_MAX);
-        CHECK(a.tiles_per_split >= 1 && a.tiles_per_split <= 256 && a.max_splits >= 1);
+        CHECK(a.tiles_per_split >= 1 && a.tiles_per_split <= 512 && a.max_splits >= 1);
       }
     }
     (void)gqa_decode_attn_noalloc(fake(4), &kv, fake_i(7), hq, 0.1f, nullptr, nullptr, fake(5),

@@ -244,13 +244,13 @@ def test_product_path_never_uses_the_oracle():
 def _planned_splits(units, max_keys, page_list, num_splits=0):
     """The split plan as documented: 16-key tiles; without an explicit count,
     chunks of at least 8 tiles sized for about 256 workgroups, at most 128
-    tiles when the chunk reads a page list and 256 otherwise."""
+    tiles when the chunk reads a page list and 512 otherwise."""
     tiles = max(1, -(-max_keys // 16))
     if num_splits > 0:
         tps = -(-tiles // num_splits)
     else:
         tps = max(-(-(units * tiles) // 256), 8)
-    tps = min(max(tps, 1), 128 if page_list else 256, tiles)
+    tps = min(max(tps, 1), 128 if page_list else 512, tiles)
     return -(-tiles // tps)
 
 
@@ -267,7 +267,7 @@ def _plan_bytes(units, splits, rows, d, k_sel=0):
 # (desc fields, Hq, budget tokens, explicit splits, page list, longest key stream, splits)
 PLAN_CASES = [
     (dict(batch=1, num_kv_heads=8, head_dim=64, capacity=4096), 32, 0, 0, False, 4096, 32),
-    (dict(batch=8, num_kv_heads=8, head_dim=128, capacity=131072), 32, 0, 0, False, 131072, 32),
+    (dict(batch=8, num_kv_heads=8, head_dim=128, capacity=131072), 32, 0, 0, False, 131072, 16),
     (dict(batch=64, num_kv_heads=8, head_dim=128, page_table=FAKE, page_size=16, max_pages=2048,
           num_pages=70000), 32, 0, 0, True, 32768, 16),
     (dict(batch=8, num_kv_heads=8, head_dim=128, capacity=131072), 32, 4096, 0, True, 4096, 4),
@@ -306,7 +306,7 @@ def test_noalloc_validation_codes(lib):
     assert _noalloc(lib, _desc(), out=0) == -1
     assert _noalloc(lib, _desc(), hq=30) == -2
     assert _noalloc(lib, _desc(batch=0), q=0, out=0) == 0
-    # 64 sequences x 8 KV heads x 2^20 keys: 256 splits of fp32 partials per
+    # 64 sequences x 8 KV heads x 2^20 keys: 128 splits of fp32 partials per
     # unit, far beyond 32 MiB
     huge = _desc(batch=64, capacity=1 << 20)
     size = ctypes.c_size_t()
