@@ -1034,7 +1034,10 @@ def long_context_line(args, torch, da, dev, flush):
         legs = {}
         for name in ("exaone30", "paged", "quest32k", "gqa1"):
             lstep, ldata = MAKERS[name](da, torch, args.seed, dev)
-            r = measure(torch, da, dev, lstep, max(10, args.steps // 2), 3, flush)
+            # half the line's steps and warm-up: with only a few warm-up steps
+            # the first timed steps of a long leg run slow while the clocks settle
+            r = measure(torch, da, dev, lstep, max(10, args.steps // 2), max(3, args.warmup // 2),
+                        flush)
             legs[name] = summarize_leg(name, lstep, r)
             if hasattr(lstep, "kernels_per_step"):
                 lf = launch_floor(torch, dev, flush, lstep.kernels_per_step, 10)
