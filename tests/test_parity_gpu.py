@@ -147,6 +147,25 @@ def test_chunk_edges_and_the_appended_slot(da, with_new, num_splits):
     assert max_err(got, want) <= ATOL
 
 
+@pytest.mark.parametrize("num_splits", [1, 2, 3])
+def test_chunks_at_the_contiguous_cap(da, num_splits):
+    """Contiguous-cache chunks of the full 512-tile cap (8192 keys; one or two
+    requested splits of 16384 keys give two such chunks) and of 342 tiles,
+    with a ragged last chunk, an appended slot that is the first key of the
+    second chunk (L = 8193) or inside a chunk, and a one-key sequence."""
+    lens = [16384, 8193, 12000, 513, 1]
+    case = workloads.dense_case(980 + num_splits, len(lens), 8, 2, 128, 16384, lens,
+                                with_new=True)
+    for b, lb in enumerate(lens):
+        case.k[b, :, lb - 1] = np.nan
+        case.v[b, :, lb - 1] = np.nan
+    got, _, _ = run_dense(da, case, num_splits=num_splits, with_new=True)
+    k2, v2 = oracle.append_kv(case.k, case.v, case.seqlens, case.k_new, case.v_new)
+    want = oracle.decode_attention(case.q, k2, v2, case.seqlens, case.scale)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, want) <= ATOL
+
+
 def test_dense_empty_and_zero_batch(da):
     case = workloads.dense_case(10, 3, 8, 2, 64, 64, [0, 5, 0])
     got, _, _ = run_dense(da, case)
