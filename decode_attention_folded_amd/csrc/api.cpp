@@ -101,24 +101,27 @@ da::SplitPlan plan_splits(const Shape& s, int max_keys, int num_splits, bool pag
   return p;
 }
 
+constexpr size_t kCounterBytes = 256;
+
 struct WsLayout {
   size_t ml, o, idx, total;
 };
 
-// Workspace: per (b, kv, split) partial softmax state (m, l) and
-// unnormalised output o, all fp32; for the selected-page stream (k_sel > 0
+// Workspace: the first 256 bytes hold the work counter of the persistent
+// paged launch (which works from any starting value, so the workspace needs
+// no initialisation); then per (b, kv, split) partial softmax state (m, l)
+// and unnormalised output o, all fp32; for the selected-page stream (k_sel > 0
 // chosen pages per unit) also room for the choice [B, Hkv, k_sel] int32,
 // which the page-selecting call fills when the unit has more pages than the
 // attention launch selects itself and the caller keeps no copy.
 WsLayout ws_layout(const Shape& s, const da::SplitPlan& p, int k_sel) {
   const size_t units = (size_t)s.batch * s.hkv;
   WsLayout w;
-  w.ml = 0;
+  w.ml = kCounterBytes;
   w.o = w.ml + align256(units * p.max_splits * s.group * 2 * sizeof(float));
   const size_t o_bytes = units * p.max_splits * s.group * s.d * sizeof(float);
   w.idx = w.o + align256(o_bytes);
   w.total = k_sel > 0 ? w.idx + units * (size_t)k_sel * sizeof(int32_t) : w.o + o_bytes;
-  if (w.total == 0) w.total = 256;
   return w;
 }
 
@@ -201,6 +204,7 @@ int run_attention(const void* q, const da_kv_cache* kv, const int32_t* seqlens,
   a.k_new = k_new;
   a.v_new = v_new;
   a.out = out;
+  a.work_counter = reinterpret_cast<uint32_t*>(ws);
   a.part_ml = reinterpret_cast<float*>(ws + w.ml);
   a.part_o = reinterpret_cast<float*>(ws + w.o);
   a.batch = s.batch;

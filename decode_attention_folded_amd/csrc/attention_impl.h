@@ -198,6 +198,54 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
   out[i] = (f16)(S > 0.0f ? O / S : 0.0f);
 }
 
+// Persistent paged dense stream (batches of at most 64 sequences).  A launch
+// of about as many workgroups as fit on the chip at once works through the
+// flat work list (see flat_chunk: real chunks only, longest sequences first,
+// the Hkv heads of a chunk on consecutive tickets).  Ticket t is the t-th
+// (chunk, head) item; workgroup w starts with ticket w and takes the next one
+// from a counter in the workspace while its current chunk still streams, then
+// loads that chunk's page-table entries, so a new chunk starts with its page
+// list already in LDS instead of three dependent memory round trips (valid
+// lengths, page table, K/V) behind the saturated HBM stream.  The hardware
+// dispatcher no longer balances the unequal sequences; the ticket order does.
+//
+// The counter needs no initial value.  It advances by the wrapping increment
+// (old >= T - 1 ? 0 : old + 1), and a launch makes exactly T fetches, T being
+// the number of tickets: one per chunk it processes.  Whatever value c the
+// counter holds when the launch starts, the T fetches return every value of
+// 0 .. T - 1 exactly once when c < T (c, c + 1, .., T - 1, 0, .., c - 1), and
+// c, 0, 1, .., T - 2 otherwise.  A fetched value v names dynamic ticket
+// grid + v when v < T - grid; the other grid values end a workgroup each.  So
+// every ticket is handed out once, and nothing a call leaves in the counter
+// changes a later call's result.
+struct Persist {
+  uint32_t* counter;          // the ticket counter (any starting value)
+  uint32_t* next_slot;        // LDS: the next ticket of this workgroup
+  int32_t* phys0_slot;        // LDS [2]: page of token 0 of each list buffer's sequence
+  const int32_t* flat_L;      // LDS [64]: clamped valid length of sequence b
+  const int32_t* flat_start;  // LDS [64]: its first flat chunk
+  const int32_t* flat_n;      // LDS [64]: its number of chunks
+  uint32_t grid;              // workgroups in the launch (= static tickets)
+  uint32_t total;             // T: flat chunks x Hkv
+  int batch;
+  int buf;                    // LDS list buffer of the current chunk
+  bool staged;                // the current chunk's list is already in that buffer
+};
+
+// Ticket t -> (split, unit) of the flat work list; wave-uniform.
+__device__ __forceinline__ void persist_lookup(const Persist& ps, int hkv, uint32_t t,
+                                               uint32_t& split_u, uint32_t& unit_u) {
+  const int lane = lane_in_wave();
+  const uint32_t f = t / (uint32_t)hkv;
+  const uint32_t kv = t - f * (uint32_t)hkv;
+  const int st = ps.flat_start[lane];
+  const int n = ps.flat_n[lane];
+  const uint64_t hit = __ballot(lane < ps.batch && (uint32_t)st <= f && f < (uint32_t)(st + n));
+  const int b = hit ? __builtin_ctzll(hit) : 0;
+  split_u = f - (uint32_t)__builtin_amdgcn_readlane(st, b);
+  unit_u = (uint32_t)b * (uint32_t)hkv + kv;
+}
+
 // The leading scalar arguments repeat the fields of `a` that the first
 // instructions need (see `launch_one`); the rest of `a` is read from the
 // kernel-argument segment while the valid-length load is in flight.  `list`
@@ -218,18 +266,31 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
 // ring's last round issues no loads past the chunk.  The arithmetic is the
 // same as without it, so both variants give bitwise equal results.
 //
+// PERSIST (paged dense stream in the persistent launch, `ps` given): the
+// valid length comes from the flat list in LDS, the chunk's page list may
+// already be staged (ps->staged), and wave 0 takes the workgroup's next ticket
+// and prepares its page list (see Persist).
+//
 // attend_chunk runs chunk `split_u` of unit `unit_u` (unit = b * Hkv + kv)
 // with the calling workgroup: it writes the unit's output when the unit has
 // one split with keys, a partial when it has more and split_u is below that
 // count, and nothing otherwise (split 0 of a unit without keys writes the
 // zero output).
-template <int D, int G, bool PAGED, bool SPARSE, int SEL_R, bool DRAIN>
+template <int D, int G, bool PAGED, bool SPARSE, int SEL_R, bool DRAIN, bool PERSIST = false>
 __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens,
                                              const void* __restrict__ q, void* k, void* v,
                                              const void* __restrict__ list, int batch, int hkv,
                                              int list_width, int chunk_geom, const AttnLaunch& a,
-                                             uint32_t split_u, uint32_t unit_u) {
+                                             uint32_t split_u, uint32_t unit_u,
+                                             Persist* ps = nullptr) {
   constexpr bool SELECT = SEL_R > 0;
+  static_assert(!PERSIST || (PAGED && !SPARSE), "the persistent launch runs the paged dense stream");
+  // The thread index, hidden from the optimiser in the persistent launch: the
+  // values derived from it are then recomputed per chunk instead of being held
+  // across the chunk loop (which took the kernel past 256 registers, half the
+  // occupancy).
+  int tid_ = (int)threadIdx.x;
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid_));
   static_assert(!SELECT || SPARSE, "page selection feeds the selected-page stream");
   static_assert(!DRAIN || !PAGED, "the draining ring is built for contiguous caches");
   static_assert(!SELECT || kThreads == kTopkThreads, "one workgroup shape for both parts");
@@ -242,11 +303,16 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
   __shared__ float s_o[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
-  __shared__ int32_t s_page[(PAGED || SPARSE) ? kMaxChunkPages : 1];
+  // chunk page lists (two in the persistent launch: the current chunk's and
+  // the next one's)
+  __shared__ int32_t s_page_mem[(PERSIST ? 2 : 1) * ((PAGED || SPARSE) ? kMaxChunkPages : 1)];
+  int32_t* s_page = s_page_mem;
+  if constexpr (PERSIST) s_page = s_page_mem + ps->buf * kMaxChunkPages;
+  const bool stage_list = !PERSIST || !ps->staged;
   __shared__ int32_t s_phys[(PAGED && SPARSE) ? kMaxChunkPages : 1];
 
-  const int lane = lane_in_wave();
-  const int wave = threadIdx.x / kWave;
+  const int lane = (tid_ & (kWave - 1));
+  const int wave = tid_ / kWave;
   const int rk = lane & 15;        // K key slot
   const int ck = lane >> 4;        // K chunk group (0..3)
   const int rv = lane & 7;         // V key slots rv, rv + 8
@@ -300,16 +366,18 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
     const float* srow = reinterpret_cast<const float*>(list) + unit * list_width;
 #pragma unroll
     for (int r = 0; r < SEL_R; ++r)
-      sel_raw[r] = early_load(srow + min(r * kThreads + (int)threadIdx.x, list_width - 1));
+      sel_raw[r] = early_load(srow + min(r * kThreads + (int)tid_, list_width - 1));
   }
 #pragma unroll
   for (int r = 0; r < kListIters; ++r) {
-    const int e = min(page0 + (int)threadIdx.x + r * kThreads, list_width - 1);
+    const int e = min(page0 + (int)tid_ + r * kThreads, list_width - 1);
     if constexpr (SPARSE) {
       raw_logical[r] = early_load(list_row + e);
     } else {
-      raw_logical[r] = page0 + (int)threadIdx.x + r * kThreads;
-      if constexpr (PAGED) raw_phys[r] = list_row[e];
+      raw_logical[r] = page0 + (int)tid_ + r * kThreads;
+      if constexpr (PAGED) {
+        if (stage_list) raw_phys[r] = list_row[e];
+      }
     }
   }
   if constexpr (PAGED && SPARSE && !SELECT) {
@@ -318,19 +386,84 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
       raw_phys[r] = a.page_table[(int64_t)b * a.max_pages + min(max(raw_logical[r], 0), a.max_pages - 1)];
   }
 
-  const StreamInfo si = stream_info(a, seqlens, b, SPARSE);
+  StreamInfo si;
+  if constexpr (PERSIST) {
+    si.L = ps->flat_L[b];
+    si.n_keys = si.L;
+    si.nsplit = ((si.L + kTileKeys - 1) / kTileKeys + a.tiles_per_split - 1) / a.tiles_per_split;
+  } else {
+    si = stream_info(a, seqlens, b, SPARSE);
+  }
   const int L = si.L;
   const int n_keys = si.n_keys;
   const int nsplit = si.nsplit;
   const int n_pages_L = (L + page_mask) >> shift;
   f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;  // rows h = G*kv + g of batch b
 
+  // Persistent launch, wave 0: the next ticket and its chunk's page list.
+  // (A paged dense chunk starts on a page boundary, so it spans at most
+  // 128 tiles x 16 keys / 8 = 256 pages: 4 entries per lane.)
+  constexpr int kNextIters = PERSIST ? kMaxTilesPerSplit * kTileKeys / kMinPageSize / kWave : 1;
+  uint32_t next_fetched = 0;          // lane 0: the counter value fetched
+  uint32_t next_ticket = 0xFFFFFFFFu; // the next ticket, or none (>= total)
+  int next_page0 = 0, next_npg = 0;
+  int next_raw[kNextIters];
+  int next_phys0 = 0;
+  auto next_fetch = [&]() {
+    if (lane == 0)
+      next_fetched = __builtin_amdgcn_atomic_inc32(ps->counter, ps->total - 1, __ATOMIC_RELAXED,
+                                                   "agent");
+  };
+  auto next_prepare = [&]() {
+    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)next_fetched, 0);
+    next_ticket = (ps->total > ps->grid && v < ps->total - ps->grid) ? ps->grid + v : 0xFFFFFFFFu;
+    if (next_ticket < ps->total) {
+      uint32_t sp, un;
+      persist_lookup(*ps, hkv, next_ticket, sp, un);
+      const int bn = (int)(un / (uint32_t)hkv);
+      const int Ln = ps->flat_L[bn];
+      const int tb = (int)sp * tiles_per_split;
+      const int te = min(tb + tiles_per_split, (Ln + kTileKeys - 1) / kTileKeys);
+      const int klast = min(te * kTileKeys, Ln) - 1;
+      next_page0 = (tb * kTileKeys) >> shift;
+      next_npg = (klast >> shift) - next_page0 + 1;
+      const int32_t* row = a.page_table + (int64_t)bn * a.max_pages;
+#pragma unroll
+      for (int r = 0; r < kNextIters; ++r)
+        next_raw[r] = row[min(next_page0 + lane + r * kWave, a.max_pages - 1)];
+      next_phys0 = row[0];
+    }
+  };
+  auto next_stage = [&]() {  // into the other list buffer, checked as below
+    if (next_ticket < ps->total) {
+      int32_t* dst = s_page_mem + (ps->buf ^ 1) * kMaxChunkPages;
+#pragma unroll
+      for (int r = 0; r < kNextIters; ++r) {
+        const int i = lane + r * kWave;
+        if (i < next_npg) {
+          int phys = next_raw[r];
+          if (next_page0 + i >= a.max_pages || phys < 0 || phys >= a.num_pages) phys = -1;
+          dst[i] = phys;
+        }
+      }
+      if (lane == 0) ps->phys0_slot[ps->buf ^ 1] = next_phys0;
+    }
+    if (lane == 0) *ps->next_slot = next_ticket;
+  };
+
   if (split >= nsplit) {
+    if constexpr (PERSIST) {
+      if (wave == 0) {
+        next_fetch();
+        next_prepare();
+        next_stage();
+      }
+    }
     if (split == 0) {  // no valid key at all: defined as a zero output
-      for (int i = threadIdx.x; i < G * D; i += kThreads) out[i] = (f16)0.0f;
+      for (int i = tid_; i < G * D; i += kThreads) out[i] = (f16)0.0f;
       if constexpr (SELECT) {  // and no page to choose
         if (a.sel_idx_out != nullptr)
-          for (int i = threadIdx.x; i < a.num_sel; i += kThreads)
+          for (int i = tid_; i < a.num_sel; i += kThreads)
             a.sel_idx_out[unit * a.num_sel + i] = -1;
       }
     }
@@ -364,7 +497,7 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
     }
     __syncthreads();
     if constexpr (PAGED) {
-      for (int i = threadIdx.x; i < npg; i += kThreads) {
+      for (int i = tid_; i < npg; i += kThreads) {
         const int logical = s_page[i];
         int phys = (logical >= 0 && logical < a.max_pages)
                        ? a.page_table[(int64_t)b * a.max_pages + logical]
@@ -375,29 +508,34 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
       __syncthreads();
     }
   } else if constexpr (PAGED || SPARSE) {
-    const int npg = (key_last >> shift) - page0 + 1;
+    if (stage_list) {
+      const int npg = (key_last >> shift) - page0 + 1;
 #pragma unroll
-    for (int r = 0; r < kListIters; ++r) {
-      const int i = (int)threadIdx.x + r * kThreads;
-      if (i < npg) {
-        int logical = raw_logical[r];
-        if constexpr (SPARSE) {
-          if (logical < 0 || logical >= n_pages_L) logical = -1;
-        }
-        int entry = logical;
-        if constexpr (PAGED) {
-          int phys = raw_phys[r];
-          if (logical < 0 || logical >= a.max_pages || phys < 0 || phys >= a.num_pages) phys = -1;
+      for (int r = 0; r < kListIters; ++r) {
+        const int i = (int)tid_ + r * kThreads;
+        if (i < npg) {
+          int logical = raw_logical[r];
           if constexpr (SPARSE) {
-            s_phys[i] = phys;
-          } else {
-            entry = phys;
+            if (logical < 0 || logical >= n_pages_L) logical = -1;
           }
+          int entry = logical;
+          if constexpr (PAGED) {
+            int phys = raw_phys[r];
+            if (logical < 0 || logical >= a.max_pages || phys < 0 || phys >= a.num_pages) phys = -1;
+            if constexpr (SPARSE) {
+              s_phys[i] = phys;
+            } else {
+              entry = phys;
+            }
+          }
+          s_page[i] = entry;
         }
-        s_page[i] = entry;
       }
+      if constexpr (PERSIST) {
+        if (tid_ == 0) ps->phys0_slot[ps->buf] = a.page_table[(int64_t)b * a.max_pages];
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // Masked keys, and the ring's loads past the chunk, read a row that holds
@@ -414,7 +552,12 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
   // row may be the slot this call is writing (L - 1)
   bool safe_is_new;
   if constexpr (PAGED) {
-    int phys0 = a.page_table[(int64_t)b * a.max_pages];
+    int phys0;
+    if constexpr (PERSIST) {
+      phys0 = ps->phys0_slot[ps->buf];
+    } else {
+      phys0 = a.page_table[(int64_t)b * a.max_pages];
+    }
     if (phys0 < 0 || phys0 >= a.num_pages) phys0 = 0;
     safe_off = (((int64_t)phys0 * hkv + kv) << shift) * D;
     safe_is_new = has_new;
@@ -463,10 +606,10 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
     } else {
       off = (unit * a.cache_stride + (L - 1)) * D;
     }
-    if (off >= 0 && threadIdx.x < 2 * (D / 8)) {
-      const int c16 = threadIdx.x % (D / 8);
-      const f16* src = (threadIdx.x < D / 8 ? knew_row : vnew_row) + 8 * c16;
-      f16* dst = reinterpret_cast<f16*>(threadIdx.x < D / 8 ? k : v) + off + 8 * c16;
+    if (off >= 0 && tid_ < 2 * (D / 8)) {
+      const int c16 = tid_ % (D / 8);
+      const f16* src = (tid_ < D / 8 ? knew_row : vnew_row) + 8 * c16;
+      f16* dst = reinterpret_cast<f16*>(tid_ < D / 8 ? k : v) + off + 8 * c16;
       *reinterpret_cast<f16x8*>(dst) = *reinterpret_cast<const f16x8*>(src);
     }
   }
@@ -598,15 +741,30 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
   {
     Stage<D> st[NS];
     const int first = tile_begin + wave;
+    // persistent launch: wave 0 takes the next ticket at the start of its
+    // second-to-last ring round and loads the next page list at the end of
+    // it (by then the fetch has returned along with that round's loads);
+    // measured equal to the last round and to the third- or fourth-to-last
+    int next_base = 0x7FFFFFFF;
+    if constexpr (PERSIST) {
+      const int rounds = (tile_end - tile_begin + NS * kWaves - 1) / (NS * kWaves);
+      if (wave == 0) next_base = tile_begin + max(rounds - 2, 0) * NS * kWaves;
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) load_stage(first + s * kWaves, st[s]);
     for (int base = first; base < tile_end; base += NS * kWaves) {
       if (!DRAIN || base + NS * kWaves < tile_end) {
+        if constexpr (PERSIST) {
+          if (base == next_base) next_fetch();
+        }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const int t = base + s * kWaves;
           if (t < tile_end) compute_stage(st[s]);
           load_stage(t + NS * kWaves, st[s]);
+        }
+        if constexpr (PERSIST) {
+          if (base == next_base) next_prepare();
         }
       } else {
         // DRAIN: the last round issues no loads past the chunk, so the code
@@ -649,12 +807,15 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
     }
   }
   __syncthreads();
+  if constexpr (PERSIST) {
+    if (wave == 0) next_stage();  // the other buffer: nobody reads it now
+  }
 
   // Merge the waves of this workgroup; write the output (single split) or
   // this split's partial.
   float* part_o = a.part_o + (unit * a.max_splits + split) * G * D;
   float* part_ml = a.part_ml + (unit * a.max_splits + split) * G * 2;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
+  for (int i = tid_; i < G * D; i += kThreads) {
     const int g = i / D;
     const int d = i % D;
     float M = s_m[0][g];
@@ -764,6 +925,97 @@ __global__ void __launch_bounds__(kThreads)
                                                   list_width, chunk_geom, a, split_u, unit_u);
 }
 
+// The persistent launch of the paged dense stream (see Persist): the flat
+// list is built once per workgroup, then the workgroup runs ticket after
+// ticket.  Every wave of a workgroup leaves the loop together (the ticket
+// comes from LDS after a barrier), and each launch ends after T fetches.
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads)
+    paged_persist_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
+                         void* v, const void* __restrict__ list, int batch, int hkv,
+                         int list_width, int chunk_geom, AttnLaunch a) {
+  __shared__ uint32_t s_next;
+  __shared__ int32_t s_phys0[2];
+  __shared__ int32_t s_fL[kWave], s_fstart[kWave], s_fn[kWave];
+  const int lane = lane_in_wave();
+  const int tps = chunk_geom & 0xFFFF;
+  // lane b: sequence b's clamped length, chunk count and first flat chunk
+  // (longest first, equal lengths in index order), as in flat_chunk
+  int L = early_load(seqlens + min(lane, batch - 1));
+  L = lane < batch ? (L < 0 ? 0 : (L > a.capacity ? a.capacity : L)) : -1;
+  int n = 0;
+  if (lane < batch) {
+    n = ((L + kTileKeys - 1) / kTileKeys + tps - 1) / tps;
+    n = n < 1 ? 1 : n;
+  }
+  int rank = 0;
+  for (int j = 0; j < batch; ++j) {
+    const int Lj = __builtin_amdgcn_readlane(L, j);
+    rank += (Lj > L || (Lj == L && j < lane)) ? 1 : 0;
+  }
+  int start = 0;
+  for (int j = 0; j < batch; ++j) {
+    const int rj = __builtin_amdgcn_readlane(rank, j);
+    const int nj = __builtin_amdgcn_readlane(n, j);
+    start += rj < rank ? nj : 0;
+  }
+  const uint32_t chunks =
+      (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan((uint32_t)n), kWave - 1);
+  if (threadIdx.x < kWave) {
+    s_fL[lane] = L;
+    s_fstart[lane] = start;
+    s_fn[lane] = n;
+  }
+  __syncthreads();
+  Persist ps;
+  ps.counter = a.work_counter;
+  ps.next_slot = &s_next;
+  ps.phys0_slot = s_phys0;
+  ps.flat_L = s_fL;
+  ps.flat_start = s_fstart;
+  ps.flat_n = s_fn;
+  ps.grid = gridDim.x;
+  ps.total = chunks * (uint32_t)hkv;
+  ps.batch = batch;
+  ps.buf = 0;
+  ps.staged = false;
+  uint32_t t = blockIdx.x;
+  if (t >= ps.total) return;
+  while (true) {
+    uint32_t split_u, unit_u;
+    persist_lookup(ps, hkv, t, split_u, unit_u);
+    attend_chunk<D, G, true, false, 0, false, true>(seqlens, q, k, v, list, batch, hkv, list_width,
+                                                    chunk_geom, a, split_u, unit_u, &ps);
+    __syncthreads();
+    t = s_next;
+    if (t >= ps.total) break;
+    ps.buf ^= 1;
+    ps.staged = true;
+  }
+}
+
+// Workgroups of the persistent launch: as many as are resident at once (its
+// register use decides how many per CU), so that no workgroup waits for
+// another to exit before it takes its first ticket.  The per-CU figure is a
+// property of the compiled kernel, looked up once.
+template <int D, int G>
+uint32_t persist_grid() {
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(paged_persist_kernel<D, G>), kThreads, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    return n;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 1;
+  return (uint32_t)(per_cu * cus);
+}
+
 // Merge kernel: one workgroup per (b, kv) unit, one thread per output element
 // of the unit's G rows (G * D threads, 64 to 1024); up to 48 splits are merged
 // with one round of loads (merge_partials).
@@ -798,7 +1050,17 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, a.seqlens, a.q, a.k, a.v, list,
                        a.batch, a.num_kv_heads, list_width, chunk_geom, a);
   };
-  if constexpr (PAGED) {
+  if constexpr (PAGED && !SPARSE && SEL_R == 0) {
+    if (a.batch <= kWave) {
+      const uint32_t tickets = (uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads;
+      const uint32_t resident = persist_grid<D, G>();
+      hipLaunchKernelGGL((paged_persist_kernel<D, G>), dim3(tickets < resident ? tickets : resident),
+                         dim3(kThreads), 0, stream, a.seqlens, a.q, a.k, a.v, list, a.batch,
+                         a.num_kv_heads, list_width, chunk_geom, a);
+    } else {
+      go(decode_kernel<D, G, true, SPARSE, SEL_R, false>);
+    }
+  } else if constexpr (PAGED) {
     go(decode_kernel<D, G, true, SPARSE, SEL_R, false>);
   } else if (drain) {
     go(decode_kernel<D, G, false, SPARSE, SEL_R, true>);

@@ -42,6 +42,9 @@ struct AttnLaunch {
   const float* sel_scores;   // [B, Hkv, sel_row] page scores, or nullptr
   int32_t* sel_idx_out;      // [B, Hkv, num_sel] or nullptr
   int32_t sel_row;           // score row width (<= 16384)
+  // Ticket counter of the persistent paged launch: the workspace's first 4
+  // bytes.  Any starting value works (attention_impl.h, Persist).
+  uint32_t* work_counter;
 };
 
 // Split plan shared by the workspace-size query and the launch.

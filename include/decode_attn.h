@@ -25,9 +25,11 @@
  *     All work is enqueued on `stream` (a hipStream_t; NULL = null stream) and
  *     is complete after the caller synchronises that stream.
  *   - Workspace: size it with da_workspace_size / da_quest_workspace_size.
- *     It holds per-split partial results (and, for one call, a page choice)
- *     only: no state survives a call, it needs no initialisation, and it must
- *     not be shared between calls that may run concurrently.
+ *     It holds per-split partial results, for one call a page choice, and a
+ *     work counter that the paged attention launch takes its chunks from
+ *     (correct from any starting value).  It needs no initialisation, nothing
+ *     a call leaves in it changes a later call's result, and it must not be
+ *     shared between calls that may run concurrently.
  *   - Return value: DA_OK or a negative DA_ERR_* code.  All argument checks run
  *     before anything is enqueued; only DA_ERR_HIP can follow a partial enqueue.
  *     The library never prints and never aborts.

@@ -146,6 +146,9 @@ void decode_checks() {
   CHECK(a.tiles_per_split >= 8 && a.max_splits * a.tiles_per_split * 16 >= 4096);
   CHECK(a.page_idx == nullptr && a.sel_scores == nullptr && a.num_sel == 0);
   CHECK(a.scale_log2 > 0.18f && a.scale_log2 < 0.181f);   // 0.125 * log2(e)
+  // the workspace: the work counter first, the partials after 256 bytes
+  CHECK(a.work_counter == reinterpret_cast<uint32_t*>(fake(6)));
+  CHECK(reinterpret_cast<const char*>(a.part_ml) == static_cast<const char*>(fake(6)) + 256);
   EXPECT_STATUS(attn(kv, 32, fake(4), fake(5), fake(6), need - 1), DA_ERR_WORKSPACE);
   // an explicit split count
   EXPECT_STATUS(attn(kv, 32, fake(4), fake(5), fake(6), kBigWs, nullptr, nullptr, 5), DA_OK);
@@ -167,7 +170,8 @@ void noalloc_checks() {
   EXPECT_STATUS(call(kv, fake(4), nullptr), DA_ERR_NULL);
   EXPECT_STATUS(call(kv, fake(4), fake(5), 30), DA_ERR_SHAPE);
   EXPECT_STATUS(call(kv, fake(4), fake(5)), DA_OK);
-  CHECK(da::g_stub.attn.part_ml == reinterpret_cast<float*>(uintptr_t(0x7f0000000000ull)));
+  CHECK(da::g_stub.attn.work_counter == reinterpret_cast<uint32_t*>(uintptr_t(0x7f0000000000ull)));
+  CHECK(da::g_stub.attn.part_ml == reinterpret_cast<float*>(uintptr_t(0x7f0000000000ull + 256)));
   da_kv_cache huge = contiguous(64, 8, 128, 1 << 20);
   EXPECT_STATUS(call(huge, fake(4), fake(5)), DA_ERR_TOO_LARGE);
 }

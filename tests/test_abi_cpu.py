@@ -255,13 +255,14 @@ def _planned_splits(units, max_keys, page_list, num_splits=0):
 
 
 def _plan_bytes(units, splits, rows, d, k_sel=0):
-    """Partials (m, l) and o; with a page budget also the choice, K int32 per
-    unit, after the 256-byte aligned partials."""
+    """The work counter's 256 bytes, then the partials (m, l) and o; with a
+    page budget also the choice, K int32 per unit, after the 256-byte aligned
+    partials."""
     ml = -(-(units * splits * rows * 2 * 4) // 256) * 256
     o = units * splits * rows * d * 4
     if k_sel == 0:
-        return ml + o
-    return ml + -(-o // 256) * 256 + units * k_sel * 4
+        return 256 + ml + o
+    return 256 + ml + -(-o // 256) * 256 + units * k_sel * 4
 
 
 # (desc fields, Hq, budget tokens, explicit splits, page list, longest key stream, splits)

@@ -702,6 +702,107 @@ def test_repeat_kv_from_paged_cache(da):
         assert np.array_equal(host(vr)[b, :, :lb], want_v[b, :, :lb])
 
 
+def _paged_items(lens, capacity, num_splits, hkv):
+    """Items of the paged flat work list for an explicit split count: chunks
+    of ceil(ceil(capacity / 16) / num_splits) 16-key tiles per sequence (one
+    for a sequence without keys), times the KV heads."""
+    tps = -(-(-(-capacity // 16)) // num_splits)
+    return hkv * sum(max(1, -(-(-(-int(l) // 16)) // tps)) for l in lens)
+
+
+def _as_i32(v):
+    return int(np.array(v, dtype=np.uint32).view(np.int32))
+
+
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_paged_counter_start_does_not_matter(da, page_size):
+    """A paged call on at most 64 sequences runs resident workgroups that take
+    their (chunk, head) items from a counter in the workspace.  With small
+    chunks (far more items than resident workgroups; 48-key chunks that do not
+    start on 64-token page boundaries), every starting value of that counter
+    -- whatever the allocation held, zero, around the item count, the largest
+    -- gives the oracle's result, bitwise the same each time: every item is
+    attended exactly once."""
+    hkv, g, d, splits = 8, 4, 128, 100
+    lens = [4096, 3001, 64, 0, 1, 2500, 17, 4000]
+    case = workloads.paged_case(270 + page_size, len(lens), hkv * g, hkv, d, page_size,
+                                4096 // page_size, lens, spare_pages=2)
+    kc = oracle.gather_paged(case.k, case.page_table, page_size, case.capacity)
+    vc = oracle.gather_paged(case.v, case.page_table, page_size, case.capacity)
+    want = oracle.decode_attention(case.q, kc, vc, case.seqlens, case.scale)
+    items = _paged_items(lens, case.capacity, splits, hkv)
+    assert items > 2 * 512
+    q, k, v, sl, pt = (dev(case.q), dev(case.k), dev(case.v), dev(case.seqlens),
+                       dev(case.page_table))
+    ws = da.Workspace()
+    first = None
+    for start in (None, 0, 1, items - 1, items, items + 1, 2**31, 2**32 - 1):
+        if start is not None:
+            ws.buf[:4].view(torch.int32).fill_(_as_i32(start))
+        out = da.gqa_decode_attn(q, k, v, sl, page_table=pt, page_size=page_size,
+                                 num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        got = host(out)
+        assert np.all(np.isfinite(got)), start
+        assert max_err(got, want) <= ATOL, start
+        if first is None:
+            first = got.copy()
+        assert np.array_equal(got.view(np.uint16), first.view(np.uint16)), start
+
+
+def test_paged_batch_above_64_sequences(da):
+    """More than 64 sequences take the flat grid of one workgroup per chunk
+    instead of the resident workgroups; against the oracle."""
+    hkv, g, d, page_size = 2, 4, 64, 16
+    lens = workloads.draw_seqlens(280, 70, 1, 700)
+    case = workloads.paged_case(281, len(lens), hkv * g, hkv, d, page_size, 700 // 16 + 1, lens)
+    got, _, _ = run_dense(da, case, num_splits=4)
+    kc = oracle.gather_paged(case.k, case.page_table, page_size, case.capacity)
+    vc = oracle.gather_paged(case.v, case.page_table, page_size, case.capacity)
+    want = oracle.decode_attention(case.q, kc, vc, case.seqlens, case.scale)
+    assert np.all(np.isfinite(got))
+    assert max_err(got, want) <= ATOL
+
+
+def test_paged_graph_replays(da):
+    """The paged call with its work counter, captured in a HIP graph and
+    replayed with eager work in between: every replay gives the eager result
+    bitwise (the counter holds a different value at each replay)."""
+    hkv, g, d, page_size, splits = 8, 4, 128, 16, 64
+    lens = [4096, 1000, 3333, 16]
+    case = workloads.paged_case(290, len(lens), hkv * g, hkv, d, page_size, 4096 // page_size,
+                                lens)
+    q, k, v, sl, pt = (dev(case.q), dev(case.k), dev(case.v), dev(case.seqlens),
+                       dev(case.page_table))
+    ws = da.Workspace()
+    out = torch.empty_like(q)
+
+    def step():
+        da.gqa_decode_attn(q, k, v, sl, page_table=pt, page_size=page_size, num_splits=splits,
+                           out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = host(out).copy()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        step()
+        stream.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+    torch.cuda.synchronize()
+    noise = torch.randn(1 << 20, device=DEV)
+    for rep in range(4):
+        out.zero_()
+        noise.mul_(1.0001).add_(1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint16), want.view(np.uint16)), rep
+
+
 def test_graph_replays_match_eager(da):
     """The calls captured in a HIP graph (dense decode with append, the fused
     Quest step with a top-K launch and sparse attention, and the Quest step
