@@ -76,14 +76,15 @@ typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kTileKeys = 16;
-// Key tiles per workgroup chunk, at most: 128 when the chunk reads a page
+// Key tiles per workgroup chunk, at most: 160 when the chunk reads a page
 // list (paged cache or chosen pages; the list is staged in LDS), 512 for a
 // contiguous cache.  Measured on MI355X: contiguous 128K dense attention
 // 672 us at 128, 642 at 256, 634 at 512, 636 at 1024 (fewer workgroup
-// start-ups and partials); the variable-length paged batch 706, 715 and
-// 761 us at 128, 256 and 512 (coarser chunks leave a longer tail of unequal
-// sequences).
-constexpr int kMaxTilesPerSplit = 128;
+// start-ups and partials); the variable-length paged batch in its persistent
+// launch 701, 686.5, 678.6, 679.5, 693.8 and 688 us at 96, 128, 160, 192, 224
+// and 256 (longer chunks mean fewer chunk changes, but a coarser tail of
+// unequal sequences).
+constexpr int kMaxTilesPerSplit = 160;
 constexpr int kMaxTilesPerSplitContiguous = 512;
 constexpr int kMinPageSize = 8;
 // pages (or chosen-page entries) one chunk can touch
@@ -401,9 +402,10 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
   f16* out = reinterpret_cast<f16*>(a.out) + unit * G * D;  // rows h = G*kv + g of batch b
 
   // Persistent launch, wave 0: the next ticket and its chunk's page list.
-  // (A paged dense chunk starts on a page boundary, so it spans at most
-  // 128 tiles x 16 keys / 8 = 256 pages: 4 entries per lane.)
-  constexpr int kNextIters = PERSIST ? kMaxTilesPerSplit * kTileKeys / kMinPageSize / kWave : 1;
+  // (A chunk starts on a 16-key tile, so it spans at most kMaxTilesPerSplit *
+  // 16 / S pages for S = 8, and at most that many plus one for S >= 16.)
+  constexpr int kNextIters =
+      PERSIST ? (kMaxTilesPerSplit * kTileKeys / kMinPageSize + kWave - 1) / kWave : 1;
   uint32_t next_fetched = 0;          // lane 0: the counter value fetched
   uint32_t next_ticket = 0xFFFFFFFFu; // the next ticket, or none (>= total)
   int next_page0 = 0, next_npg = 0;

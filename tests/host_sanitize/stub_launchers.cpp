@@ -15,7 +15,7 @@ namespace da {
 StubRecord g_stub;
 
 int keys_per_tile(int, int) { return 16; }
-int max_tiles_per_split(bool page_list) { return page_list ? 128 : 512; }
+int max_tiles_per_split(bool page_list) { return page_list ? 160 : 512; }
 int topk_max_pages() { return 256 * 64; }
 size_t noalloc_scratch_bytes() { return size_t(32) << 20; }
 int noalloc_scratch(void** ptr) {

@@ -243,14 +243,14 @@ def test_product_path_never_uses_the_oracle():
 
 def _planned_splits(units, max_keys, page_list, num_splits=0):
     """The split plan as documented: 16-key tiles; without an explicit count,
-    chunks of at least 8 tiles sized for about 256 workgroups, at most 128
+    chunks of at least 8 tiles sized for about 256 workgroups, at most 160
     tiles when the chunk reads a page list and 512 otherwise."""
     tiles = max(1, -(-max_keys // 16))
     if num_splits > 0:
         tps = -(-tiles // num_splits)
     else:
         tps = max(-(-(units * tiles) // 256), 8)
-    tps = min(max(tps, 1), 128 if page_list else 512, tiles)
+    tps = min(max(tps, 1), 160 if page_list else 512, tiles)
     return -(-tiles // tps)
 
 
@@ -270,7 +270,7 @@ PLAN_CASES = [
     (dict(batch=1, num_kv_heads=8, head_dim=64, capacity=4096), 32, 0, 0, False, 4096, 32),
     (dict(batch=8, num_kv_heads=8, head_dim=128, capacity=131072), 32, 0, 0, False, 131072, 16),
     (dict(batch=64, num_kv_heads=8, head_dim=128, page_table=FAKE, page_size=16, max_pages=2048,
-          num_pages=70000), 32, 0, 0, True, 32768, 16),
+          num_pages=70000), 32, 0, 0, True, 32768, 13),
     (dict(batch=8, num_kv_heads=8, head_dim=128, capacity=131072), 32, 4096, 0, True, 4096, 4),
     (dict(batch=1, num_kv_heads=32, head_dim=128, capacity=32768), 32, 2048, 0, True, 2048, 8),
     (dict(batch=2, num_kv_heads=8, head_dim=128, capacity=4096), 32, 0, 7, False, 4096, 7),
