@@ -166,7 +166,7 @@ def paged(da, torch, seed, dev):
     cfg = {"workload": "paged_gqa_decode_b64_hq32_hkv8_d128_s16_len1k-32k", "batch": b,
            "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "page_size": s,
            "total_tokens": int(np.sum(lens))}
-    st = Stage("attention", [one], per, "decode_kernel + merge_kernel (gqa_decode_attn)")
+    st = Stage("attention", [one], per, "paged_persist_kernel + merge_kernel (gqa_decode_attn)")
     return Step("paged", cfg, kv, per, [st]), c
 
 
