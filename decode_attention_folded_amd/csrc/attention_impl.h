@@ -221,7 +221,7 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
 // changes a later call's result.
 struct Persist {
   uint32_t* counter;          // the ticket counter (any starting value)
-  uint32_t* next_slot;        // LDS: the next ticket of this workgroup
+  uint32_t* next_slot;        // LDS [2]: the ticket after each buffer's chunk
   int32_t* phys0_slot;        // LDS [2]: page of token 0 of each list buffer's sequence
   const int32_t* flat_L;      // LDS [64]: clamped valid length of sequence b
   const int32_t* flat_start;  // LDS [64]: its first flat chunk
@@ -450,7 +450,9 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
       }
       if (lane == 0) ps->phys0_slot[ps->buf ^ 1] = next_phys0;
     }
-    if (lane == 0) *ps->next_slot = next_ticket;
+    // (double-buffered like the lists: a chunk without keys writes this
+    // before any barrier, while other waves may still read the last value)
+    if (lane == 0) ps->next_slot[ps->buf ^ 1] = next_ticket;
   };
 
   if (split >= nsplit) {
@@ -936,7 +938,7 @@ __global__ void __launch_bounds__(kThreads)
     paged_persist_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
                          void* v, const void* __restrict__ list, int batch, int hkv,
                          int list_width, int chunk_geom, AttnLaunch a) {
-  __shared__ uint32_t s_next;
+  __shared__ uint32_t s_next[2];
   __shared__ int32_t s_phys0[2];
   __shared__ int32_t s_fL[kWave], s_fstart[kWave], s_fn[kWave];
   const int lane = lane_in_wave();
@@ -971,7 +973,7 @@ __global__ void __launch_bounds__(kThreads)
   __syncthreads();
   Persist ps;
   ps.counter = a.work_counter;
-  ps.next_slot = &s_next;
+  ps.next_slot = s_next;
   ps.phys0_slot = s_phys0;
   ps.flat_L = s_fL;
   ps.flat_start = s_fstart;
@@ -989,7 +991,7 @@ __global__ void __launch_bounds__(kThreads)
     attend_chunk<D, G, true, false, 0, false, true>(seqlens, q, k, v, list, batch, hkv, list_width,
                                                     chunk_geom, a, split_u, unit_u, &ps);
     __syncthreads();
-    t = s_next;
+    t = s_next[ps.buf ^ 1];
     if (t >= ps.total) break;
     ps.buf ^= 1;
     ps.staged = true;
