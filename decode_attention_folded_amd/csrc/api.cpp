@@ -108,8 +108,8 @@ struct WsLayout {
 };
 
 // Workspace: the first 256 bytes hold the work counter of the persistent
-// paged launch (which works from any starting value, so the workspace needs
-// no initialisation); then per (b, kv, split) partial softmax state (m, l)
+// paged launch (cleared by the call before that launch, so the workspace
+// needs no initialisation); then per (b, kv, split) partial softmax state (m, l)
 // and unnormalised output o, all fp32; for the selected-page stream (k_sel > 0
 // chosen pages per unit) also room for the choice [B, Hkv, k_sel] int32,
 // which the page-selecting call fills when the unit has more pages than the

@@ -210,17 +210,16 @@ __device__ __forceinline__ void merge_partials(const AttnLaunch& a, const float*
 // lengths, page table, K/V) behind the saturated HBM stream.  The hardware
 // dispatcher no longer balances the unequal sequences; the ticket order does.
 //
-// The counter needs no initial value.  It advances by the wrapping increment
-// (old >= T - 1 ? 0 : old + 1), and a launch makes exactly T fetches, T being
-// the number of tickets: one per chunk it processes.  Whatever value c the
-// counter holds when the launch starts, the T fetches return every value of
-// 0 .. T - 1 exactly once when c < T (c, c + 1, .., T - 1, 0, .., c - 1), and
-// c, 0, 1, .., T - 2 otherwise.  A fetched value v names dynamic ticket
-// grid + v when v < T - grid; the other grid values end a workgroup each.  So
-// every ticket is handed out once, and nothing a call leaves in the counter
-// changes a later call's result.
+// The counter starts at zero: a one-thread launch clears it just before (the
+// workspace itself needs no initialisation).  A fetched value v names ticket
+// grid + v when v < T - grid, T being the number of tickets; any other value
+// ends the workgroup.  Values come in increasing order, so every valid one is
+// handed out before the first that ends a workgroup, and every ticket is
+// processed exactly once.  (From an arbitrary starting value that fails: the
+// values that end workgroups can come first and stop them all before the low
+// values are handed out.)
 struct Persist {
-  uint32_t* counter;          // the ticket counter (any starting value)
+  uint32_t* counter;          // the ticket counter (zero at the launch)
   uint32_t* next_slot;        // LDS [2]: the ticket after each buffer's chunk
   int32_t* phys0_slot;        // LDS [2]: page of token 0 of each list buffer's sequence
   const int32_t* flat_L;      // LDS [64]: clamped valid length of sequence b
@@ -413,8 +412,8 @@ __device__ __forceinline__ void attend_chunk(const int32_t* __restrict__ seqlens
   int next_phys0 = 0;
   auto next_fetch = [&]() {
     if (lane == 0)
-      next_fetched = __builtin_amdgcn_atomic_inc32(ps->counter, ps->total - 1, __ATOMIC_RELAXED,
-                                                   "agent");
+      next_fetched = __hip_atomic_fetch_add(ps->counter, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
   };
   auto next_prepare = [&]() {
     const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)next_fetched, 0);
@@ -932,7 +931,9 @@ __global__ void __launch_bounds__(kThreads)
 // The persistent launch of the paged dense stream (see Persist): the flat
 // list is built once per workgroup, then the workgroup runs ticket after
 // ticket.  Every wave of a workgroup leaves the loop together (the ticket
-// comes from LDS after a barrier), and each launch ends after T fetches.
+// comes from LDS after a barrier); a workgroup ends at its first fetched
+// value past the tickets, which every workgroup reaches after at most T
+// fetches in all.
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads)
     paged_persist_kernel(const int32_t* __restrict__ seqlens, const void* __restrict__ q, void* k,
@@ -998,6 +999,12 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// Clears the work counter of the persistent launch (a kernel rather than a
+// memset, so that a captured graph replays it as such).
+__global__ void __launch_bounds__(kWave) counter_clear_kernel(uint32_t* counter) {
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workgroups of the persistent launch: as many as are resident at once (its
 // register use decides how many per CU), so that no workgroup waits for
 // another to exit before it takes its first ticket.  The per-CU figure is a
@@ -1055,12 +1062,15 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
                        a.batch, a.num_kv_heads, list_width, chunk_geom, a);
   };
   if constexpr (PAGED && !SPARSE && SEL_R == 0) {
-    if (a.batch <= kWave) {
-      const uint32_t tickets = (uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads;
-      const uint32_t resident = persist_grid<D, G>();
-      hipLaunchKernelGGL((paged_persist_kernel<D, G>), dim3(tickets < resident ? tickets : resident),
-                         dim3(kThreads), 0, stream, a.seqlens, a.q, a.k, a.v, list, a.batch,
-                         a.num_kv_heads, list_width, chunk_geom, a);
+    // The persistent launch where the work list can outnumber the resident
+    // workgroups (at most 64 sequences); otherwise one workgroup per item.
+    const uint32_t tickets = (uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads;
+    const uint32_t resident = a.batch <= kWave ? persist_grid<D, G>() : 0u;
+    if (tickets > resident && a.batch <= kWave) {
+      hipLaunchKernelGGL(counter_clear_kernel, dim3(1), dim3(kWave), 0, stream, a.work_counter);
+      hipLaunchKernelGGL((paged_persist_kernel<D, G>), dim3(resident), dim3(kThreads), 0, stream,
+                         a.seqlens, a.q, a.k, a.v, list, a.batch, a.num_kv_heads, list_width,
+                         chunk_geom, a);
     } else {
       go(decode_kernel<D, G, true, SPARSE, SEL_R, false>);
     }

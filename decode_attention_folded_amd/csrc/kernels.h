@@ -43,7 +43,7 @@ struct AttnLaunch {
   int32_t* sel_idx_out;      // [B, Hkv, num_sel] or nullptr
   int32_t sel_row;           // score row width (<= 16384)
   // Ticket counter of the persistent paged launch: the workspace's first 4
-  // bytes.  Any starting value works (attention_impl.h, Persist).
+  // bytes, cleared by the call before that launch (attention_impl.h, Persist).
   uint32_t* work_counter;
 };
 

@@ -27,9 +27,9 @@
  *   - Workspace: size it with da_workspace_size / da_quest_workspace_size.
  *     It holds per-split partial results, for one call a page choice, and a
  *     work counter that the paged attention launch takes its chunks from
- *     (correct from any starting value).  It needs no initialisation, nothing
- *     a call leaves in it changes a later call's result, and it must not be
- *     shared between calls that may run concurrently.
+ *     (the call clears it first).  It needs no initialisation, nothing a call
+ *     leaves in it changes a later call's result, and it must not be shared
+ *     between calls that may run concurrently.
  *   - Return value: DA_OK or a negative DA_ERR_* code.  All argument checks run
  *     before anything is enqueued; only DA_ERR_HIP can follow a partial enqueue.
  *     The library never prints and never aborts.

@@ -717,12 +717,14 @@ def _as_i32(v):
 @pytest.mark.parametrize("page_size", [16, 64])
 def test_paged_counter_start_does_not_matter(da, page_size):
     """A paged call on at most 64 sequences runs resident workgroups that take
-    their (chunk, head) items from a counter in the workspace.  With small
-    chunks (far more items than resident workgroups; 48-key chunks that do not
-    start on 64-token page boundaries), every starting value of that counter
-    -- whatever the allocation held, zero, around the item count, the largest
-    -- gives the oracle's result, bitwise the same each time: every item is
-    attended exactly once."""
+    their (chunk, head) items from a counter in the workspace, which the call
+    clears first.  With small chunks (far more items than resident
+    workgroups; 48-key chunks that do not start on 64-token page boundaries),
+    whatever the counter holds before the call -- what the allocation held,
+    zero, around the item count, the largest value -- the result is the
+    oracle's, bitwise the same each time.  The split partials are poisoned
+    with NaN before every call, so a chunk that no workgroup attended would
+    show instead of reusing the previous call's partial."""
     hkv, g, d, splits = 8, 4, 128, 100
     lens = [4096, 3001, 64, 0, 1, 2500, 17, 4000]
     case = workloads.paged_case(270 + page_size, len(lens), hkv * g, hkv, d, page_size,
@@ -739,6 +741,7 @@ def test_paged_counter_start_does_not_matter(da, page_size):
     for start in (None, 0, 1, items - 1, items, items + 1, 2**31, 2**32 - 1):
         if start is not None:
             ws.buf[:4].view(torch.int32).fill_(_as_i32(start))
+            ws.buf[256:].fill_(0xFF)  # NaN in every partial
         out = da.gqa_decode_attn(q, k, v, sl, page_table=pt, page_size=page_size,
                                  num_splits=splits, workspace=ws)
         torch.cuda.synchronize()
@@ -766,8 +769,8 @@ def test_paged_batch_above_64_sequences(da):
 
 def test_paged_graph_replays(da):
     """The paged call with its work counter, captured in a HIP graph and
-    replayed with eager work in between: every replay gives the eager result
-    bitwise (the counter holds a different value at each replay)."""
+    replayed with eager work in between (which also poisons the split
+    partials): every replay gives the eager result bitwise."""
     hkv, g, d, page_size, splits = 8, 4, 128, 16, 64
     lens = [4096, 1000, 3333, 16]
     case = workloads.paged_case(290, len(lens), hkv * g, hkv, d, page_size, 4096 // page_size,
@@ -796,6 +799,7 @@ def test_paged_graph_replays(da):
     noise = torch.randn(1 << 20, device=DEV)
     for rep in range(4):
         out.zero_()
+        ws.buf[256:].fill_(0xFF)
         noise.mul_(1.0001).add_(1.0)
         torch.cuda.synchronize()
         graph.replay()
