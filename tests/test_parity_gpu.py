@@ -753,6 +753,38 @@ def test_paged_counter_start_does_not_matter(da, page_size):
         assert np.array_equal(got.view(np.uint16), first.view(np.uint16)), start
 
 
+@pytest.mark.parametrize("page_size", [8, 32])
+@pytest.mark.parametrize("d,g", [(64, 1), (64, 2), (64, 4), (64, 8), (128, 1), (128, 2),
+                                 (128, 4), (128, 8)])
+def test_paged_persistent_launch_shapes(da, d, g, page_size):
+    """Every (D, rows) instantiation of the persistent paged launch, forced by
+    many small chunks (64 splits per sequence: more (chunk, head) items than
+    resident workgroups, so some come from the work counter), against the
+    oracle; ragged lengths, a sequence
+    without keys, chunks not aligned to 32-token pages, NaN in unused pool
+    pages and in every split partial before the call."""
+    hkv, splits = 8, 64  # 1,712 items; at most 1,024 resident workgroups (4 per CU)
+    lens = [4096, 2047, 0, 3333, 1, 4000]
+    case = workloads.paged_case(300 + d + g + page_size, len(lens), hkv * g, hkv, d, page_size,
+                                4096 // page_size, lens, spare_pages=3)
+    assert _paged_items(lens, case.capacity, splits, hkv) > 1024
+    kc = oracle.gather_paged(case.k, case.page_table, page_size, case.capacity)
+    vc = oracle.gather_paged(case.v, case.page_table, page_size, case.capacity)
+    want = oracle.decode_attention(case.q, kc, vc, case.seqlens, case.scale)
+    q, k, v, sl, pt = (dev(case.q), dev(case.k), dev(case.v), dev(case.seqlens),
+                       dev(case.page_table))
+    ws = da.Workspace()
+    for rep in range(2):
+        if rep:
+            ws.buf[256:].fill_(0xFF)  # NaN in every partial
+        out = da.gqa_decode_attn(q, k, v, sl, page_table=pt, page_size=page_size,
+                                 num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        got = host(out)
+        assert np.all(np.isfinite(got)), rep
+        assert max_err(got, want) <= ATOL, rep
+
+
 def test_paged_batch_above_64_sequences(da):
     """More than 64 sequences take the flat grid of one workgroup per chunk
     instead of the resident workgroups; against the oracle."""
