@@ -1055,8 +1055,13 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
   // Short chunks of a contiguous cache (at most two ring rounds per wave,
   // such as a few thousand keys split over the chip) use the draining ring;
   // long chunks keep the plain one (the drain measured 1.5% slower on them),
-  // and so does the paged cache (10% slower with it).
-  const bool drain = !PAGED && a.tiles_per_split <= 2 * kStages * kWaves;
+  // and so does the paged cache (10% slower with it).  With 8 rows of D = 128
+  // the draining ring does not fit in registers (the compiler spilled 170 to
+  // 280 of them to scratch memory) and is not built: the plain ring, at 325
+  // registers, measured 2.2x faster on such chunks (G = 8 at 4096 keys:
+  // 43.2 -> 19.3 us).
+  constexpr bool kDrainFits = !(D == 128 && G == 8);
+  const bool drain = kDrainFits && !PAGED && a.tiles_per_split <= 2 * kStages * kWaves;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, a.seqlens, a.q, a.k, a.v, list,
                        a.batch, a.num_kv_heads, list_width, chunk_geom, a);
@@ -1077,7 +1082,7 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
   } else if constexpr (PAGED) {
     go(decode_kernel<D, G, true, SPARSE, SEL_R, false>);
   } else if (drain) {
-    go(decode_kernel<D, G, false, SPARSE, SEL_R, true>);
+    if constexpr (kDrainFits) go(decode_kernel<D, G, false, SPARSE, SEL_R, true>);
   } else {
     go(decode_kernel<D, G, false, SPARSE, SEL_R, false>);
   }
