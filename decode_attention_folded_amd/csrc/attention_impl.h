@@ -1066,9 +1066,16 @@ int launch_one(const AttnLaunch& a, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, a.seqlens, a.q, a.k, a.v, list,
                        a.batch, a.num_kv_heads, list_width, chunk_geom, a);
   };
-  if constexpr (PAGED && !SPARSE && SEL_R == 0) {
-    // The persistent launch where the work list can outnumber the resident
-    // workgroups (at most 64 sequences); otherwise one workgroup per item.
+  // The persistent launch of the paged dense stream pays where the rows times
+  // the head dimension reach 512 (4 rows of D = 128, 8 of D = 64): it measured 1.5%
+  // faster at D = 128, G = 4, 13.5% at D = 128, G = 8 and 8% at D = 64, G = 8
+  // on the batch of 64 (lengths 1K-32K), and equal or 1-3% slower than one
+  // workgroup per chunk below that (more workgroups fit on a CU there, and
+  // the hardware dispatcher hides their start-up).
+  constexpr bool kPersistent = PAGED && !SPARSE && SEL_R == 0 && G * D >= 512;
+  if constexpr (kPersistent) {
+    // where the work list can outnumber the resident workgroups (at most 64
+    // sequences); otherwise one workgroup per item
     const uint32_t tickets = (uint32_t)a.max_splits * (uint32_t)a.batch * (uint32_t)a.num_kv_heads;
     const uint32_t resident = a.batch <= kWave ? persist_grid<D, G>() : 0u;
     if (tickets > resident && a.batch <= kWave) {

@@ -757,10 +757,10 @@ def test_paged_counter_start_does_not_matter(da, page_size):
 @pytest.mark.parametrize("d,g", [(64, 1), (64, 2), (64, 4), (64, 8), (128, 1), (128, 2),
                                  (128, 4), (128, 8)])
 def test_paged_persistent_launch_shapes(da, d, g, page_size):
-    """Every (D, rows) instantiation of the persistent paged launch, forced by
-    many small chunks (64 splits per sequence: more (chunk, head) items than
-    resident workgroups, so some come from the work counter), against the
-    oracle; ragged lengths, a sequence
+    """Every (D, rows) combination of the paged dense stream with many small
+    chunks (64 splits per sequence: more (chunk, head) items than resident
+    workgroups; where rows * D >= 512 the persistent launch runs and some
+    items come from the work counter), against the oracle; ragged lengths, a sequence
     without keys, chunks not aligned to 32-token pages, NaN in unused pool
     pages and in every split partial before the call."""
     hkv, splits = 8, 64  # 1,712 items; at most 1,024 resident workgroups (4 per CU)
