@@ -18,7 +18,11 @@
 // Work decomposition (flash-decode): a 1-D grid of splits x (B * Hkv) units,
 // unit index fastest.  A workgroup of 4 waves owns a contiguous chunk of
 // `tiles_per_split` 16-key tiles of one (b, kv) unit; its waves take the
-// chunk's tiles round robin.  Workgroups reach the 8 XCDs round robin, so with
+// chunk's tiles round robin.  (The paged dense stream instead takes its
+// chunks from a flat list of real chunks, longest sequences first: one
+// workgroup per chunk, or, for up to 64 sequences with rows x D >= 512,
+// resident workgroups that take chunk after chunk from a work counter; see
+// flat_chunk and Persist.)  Workgroups reach the 8 XCDs round robin, so with
 // the unit index fastest every XCD receives the same KV heads of every
 // sequence: sequences of different lengths load the XCDs evenly, which they
 // do not when the split index runs fastest (short sequences would only feed
